@@ -1,0 +1,152 @@
+/*
+ * fa.h -- FlashAttention forward pass and split-KV decode for AMD Instinct MI355X (gfx950).
+ *
+ * C linkage; no C++ or framework types cross this boundary.  Every tensor argument is a
+ * DEVICE pointer owned by the caller.  The library never allocates, frees or synchronises:
+ * each call validates its arguments, enqueues its kernels on `stream` and returns.  Outputs
+ * are valid once the stream reaches the enqueued work; inputs must stay alive until then.
+ * There is no global mutable state, so calls from several host threads are safe.
+ *
+ * Layouts (all contiguous, head dimension fastest, as the Flash Attention 1 kernel of the
+ * page "Kernel visualization: Flash Attention 1" ("Initial setup") offsets its pointers by
+ * batch*head*N*D):
+ *   Q, O            [B, H_q,  N_q, d]          (decode: N_q = T new queries)
+ *   K, V            [B, H_kv, N_k, d]          (contiguous cache)
+ *   K, V pools      [num_pages, page_size, H_kv, d]   (paged cache, decode only)
+ *   LSE             [B, H_q, N_q] fp32
+ *   block_table     [B, pages_per_seq] int32
+ *
+ * Semantics (each output row is exact attention up to rounding):
+ *   x_j   = scale * <Q[b,h,i,:], K[b,h_kv,j,:]>,  h_kv = h / (H_q / H_kv)
+ *           (GQA: contiguous groups of H_q/H_kv query heads share one KV head; page
+ *            "Attention kernel chains", chain "GQA loads KV once per group")
+ *   visible keys: all j < N_k, or with causal != 0 only j <= i + (N_k - N_q): the mask is
+ *           aligned to the bottom-right corner, query row i sits at position N_k - N_q + i
+ *           (chain "The causal mask for a decode step")
+ *   O[b,h,i,:] = sum_j p_j V[b,h_kv,j,:],  p = softmax of the visible x
+ *           (page "Kernel visualization: Flash Attention 1", "Derivation")
+ *   LSE[b,h,i] = ln sum_j e^{x_j}  over visible j  (natural log of the scaled scores; chain
+ *           "What the backward pass saves": one fp32 log-sum-exp per query row)
+ *   A row with no visible key (causal with N_q > N_k) gets O = 0 and LSE = -inf.
+ *
+ * Errors: arguments are validated before anything is enqueued; on any failure nothing is
+ * enqueued and a non-zero fa_status is returned.  A failed launch returns FA_ERR_HIP.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,    /* a size is <= 0, H_q % H_kv != 0, scale not > 0, bad split/page args */
+  FA_ERR_UNSUPPORTED = 3,  /* head dimension or dtype the library has no kernel for */
+  FA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than fa_decode_workspace_bytes() */
+  FA_ERR_ALIGNMENT = 5,    /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_BF16 = 0,             /* bf16 Q/K/V and O; fp32 accumulation and LSE */
+  FA_FP32 = 1,             /* fp32 Q/K/V and O (fa_fwd only) */
+  FA_BF16_IN_FP32_OUT = 2  /* bf16 Q/K/V, O stored as fp32 before any rounding to bf16 */
+} fa_dtype;
+
+/*
+ * fa_fwd -- the FlashAttention forward pass in FlashAttention-2 loop order.
+ *
+ * Defined by: page "Softmax and FlashAttention" ("Concept": a block of Br queries, K and V
+ * streamed past in blocks of Bc, each Br x Bc score tile computed on chip and folded into
+ * a running output) with the online-softmax carries of page "Kernel visualization: Flash
+ * Attention 1" ("Derivation", "The tiled version": running max, running sum, unnormalized
+ * accumulator) and the single division at the end (page "Attention kernel chains", chain
+ * "The online softmax on numbers").
+ *
+ *   Q [B,H_q,N_q,d], K/V [B,H_kv,N_k,d] in `dtype`'s input type; O [B,H_q,N_q,d] in its
+ *   output type; LSE [B,H_q,N_q] fp32 (may be NULL if not wanted).
+ *   d in {64, 128}.  scale > 0 (typically 1/sqrt(d)).  causal: 0 or 1 (bottom-right).
+ *   N_q, N_k >= 1, any value (ragged tails are masked).  stream: a hipStream_t or NULL.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int B, int H_q, int H_kv, int N_q, int N_k, int d,
+           float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_decode_num_splits -- the split count fa_decode_splitkv uses when called with
+ * num_splits == 0.  Splitting pays when batch x KV heads is far below the number of
+ * compute units; the aim is about one full wave of workgroups and no mostly idle second
+ * wave (page "Attention kernel chains", chain "How many splits for decode"), here for the
+ * MI355X's 256 compute units.  Returns >= 1, or 0 on invalid sizes.
+ */
+int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d);
+
+/*
+ * fa_decode_workspace_bytes -- bytes of device workspace fa_decode_splitkv needs for
+ * `num_splits` splits (0 = the automatic count): the normalized partial outputs
+ * O_part [ns, B*H_q*T, d] fp32 followed by LSE_part [ns, B*H_q*T] fp32, each part 256-byte
+ * aligned.  Returns 0 when num_splits resolves to 1 (no workspace needed) or on bad sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d, int num_splits);
+
+/*
+ * fa_decode_splitkv -- split-KV ("flash decoding") attention of T new queries over a cache
+ * of N_k keys, with the partial results combined by the LSE merge.
+ *
+ * Defined by: page "Attention kernel chains", chains "How many splits for decode" (the key
+ * axis is cut into num_splits contiguous chunks, one worker each), "The log-sum-exp merge"
+ * (each worker writes a normalized partial output and its lse; any split is exact), "GQA
+ * loads KV once per group" (the H_q/H_kv query heads of a group are stacked as the rows of
+ * one tile so each KV tile is read once per group) and "The block-table cost of paged
+ * attention" (one int32 page index per page_size-token block).
+ *
+ *   Q [B,H_q,T,d] bf16; O [B,H_q,T,d] bf16 (FA_BF16) or fp32 (FA_BF16_IN_FP32_OUT);
+ *   LSE [B,H_q,T] fp32 (may be NULL).
+ *   block_table == NULL: K/V contiguous [B,H_kv,N_k,d] bf16.
+ *   block_table != NULL: K/V pools [num_pages,page_size,H_kv,d] bf16; token j of sequence b
+ *     is in page block_table[b*pages_per_seq + j/page_size], slot j%page_size; requires
+ *     page_size >= 1 and pages_per_seq*page_size >= N_k.  Table contents are not checked:
+ *     an entry outside the pool is undefined behaviour, as in any gather.
+ *   causal: 0 (every cached key visible) or 1 (bottom-right: query t sees j <= N_k - T + t).
+ *   num_splits: >= 1, or 0 for fa_decode_num_splits().  Splits are contiguous key ranges of
+ *     equal length rounded up to 64 keys; trailing splits may be empty.
+ *   workspace: >= fa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
+ *     that is 0).  d == 128 or 64.
+ */
+int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      int B, int H_q, int H_kv, int T, int N_k, int d,
+                      float scale, int causal, int num_splits,
+                      const int32_t* block_table, int page_size, int pages_per_seq,
+                      void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_lse_merge -- combine normalized partial results over disjoint key sets.
+ *
+ * Defined by: page "Attention kernel chains", chain "The log-sum-exp merge":
+ *   lse = ln sum_s e^{lse_s},   O = sum_s e^{lse_s - lse} O_s,
+ * computed against m* = max_s lse_s.  Partials with lse_s = -inf (a worker that saw no
+ * key) get weight 0; a row whose partials are all -inf gets O = 0 and lse = -inf.
+ *
+ *   O_part [num_splits, rows, d] fp32, LSE_part [num_splits, rows] fp32 (the workspace
+ *   layout of fa_decode_splitkv); O [rows, d] in out_dtype (FA_BF16 or FA_FP32);
+ *   LSE [rows] fp32 (may be NULL).  num_splits >= 1, rows >= 1, 1 <= d <= 512.
+ */
+int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE,
+                 int num_splits, int rows, int d, int out_dtype, void* stream);
+
+/* Human-readable name of an fa_status value (static storage; never NULL). */
+const char* fa_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,141 @@
+// The C ABI declared in include/fa.h: argument validation, kernel selection and launch
+// on the caller's stream.  Nothing here allocates, frees or synchronises, and every check
+// runs before the first HIP call, so an invalid call enqueues nothing.
+#include <math.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kNumCU = 256;        // MI355X compute units
+constexpr int kDecodeWGPerCU = 2;  // decode workgroups resident per CU (LDS/VGPR bound)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int check_heads(int B, int H_q, int H_kv, int n_q, int n_k, int d) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || n_q < 1 || n_k < 1 || d < 1) return FA_ERR_BAD_SHAPE;
+  if (H_q % H_kv != 0) return FA_ERR_BAD_SHAPE;
+  // every element index must fit the 64-bit offsets and every row index a 32-bit int
+  if ((long long)B * H_q * n_q > 0x7fffffffLL || (long long)B * H_kv * n_k > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  return FA_OK;
+}
+
+// Keys per split: ceil(N_k / ns) rounded up to the decode chunk.
+int split_len_of(int n_k, int ns) {
+  const long long per = ((long long)n_k + ns - 1) / ns;
+  return (int)((per + fa::kDecodeChunk - 1) / fa::kDecodeChunk * fa::kDecodeChunk);
+}
+
+int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
+  const long long row_chunks = ((long long)(H_q / H_kv) * T + 15) / 16;
+  const long long base = (long long)B * H_kv * row_chunks;  // workgroups without splitting
+  const long long target = (long long)kNumCU * kDecodeWGPerCU;
+  long long ns = base >= target ? 1 : target / base;
+  const long long max_useful = ((long long)N_k + 4 * fa::kDecodeChunk - 1) / (4 * fa::kDecodeChunk);
+  if (ns > max_useful) ns = max_useful;  // at least one chunk per wave
+  if (ns < 1) ns = 1;
+  return (int)ns;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: invalid size, head grouping, scale, split or page argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension or dtype not supported";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_ALIGNMENT: return "FA_ERR_ALIGNMENT: tensor pointer not 16-byte aligned";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
+           int N_q, int N_k, int d, float scale, int causal, int dtype, void* stream) {
+  if (!Q || !K || !V || !O) return FA_ERR_NULL_PTR;
+  int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
+  if (st != FA_OK) return st;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP32 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)))
+    return FA_ERR_ALIGNMENT;
+  fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
+  if (dtype == FA_FP32) return status_of(fa::launch_fwd_fp32(a));
+  return status_of(fa::launch_fwd_bf16(a, dtype == FA_BF16_IN_FP32_OUT));
+}
+
+int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d) {
+  if (check_heads(B, H_q, H_kv, T, N_k, d) != FA_OK) return 0;
+  return auto_splits(B, H_q, H_kv, T, N_k);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d, int num_splits) {
+  if (check_heads(B, H_q, H_kv, T, N_k, d) != FA_OK || num_splits < 0) return 0;
+  const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)B * H_q * T;
+  return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float));
+}
+
+int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q,
+                      int H_kv, int T, int N_k, int d, float scale, int causal, int num_splits,
+                      const int32_t* block_table, int page_size, int pages_per_seq, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  if (!Q || !K || !V || !O) return FA_ERR_NULL_PTR;
+  int st = check_heads(B, H_q, H_kv, T, N_k, d);
+  if (st != FA_OK) return st;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1) || num_splits < 0) return FA_ERR_BAD_SHAPE;
+  if (block_table != nullptr) {
+    if (page_size < 1 || pages_per_seq < 1 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
+    if ((long long)B * pages_per_seq > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  }
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H_kv > 65535 || ((long long)(H_q / H_kv) * T + 15) / 16 > 65535) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)) ||
+      (block_table && !aligned4(block_table)))
+    return FA_ERR_ALIGNMENT;
+  const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
+  const size_t need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGNMENT;
+
+  const size_t rows = (size_t)B * H_q * T;
+  float* O_part = nullptr;
+  float* LSE_part = nullptr;
+  if (ns > 1) {
+    O_part = static_cast<float*>(workspace);
+    LSE_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)ns * rows * d * sizeof(float)));
+  }
+  fa::DecodeArgs a{Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, ns, split_len_of(N_k, ns),
+                   block_table, page_size, pages_per_seq, O_part, LSE_part, stream};
+  const bool out_f32 = dtype == FA_BF16_IN_FP32_OUT;
+  hipError_t e = fa::launch_decode_split(a, out_f32);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  if (ns > 1) e = fa::launch_lse_merge(O_part, LSE_part, O, LSE, ns, (int)rows, d, out_f32, stream);
+  return status_of(e);
+}
+
+int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE, int num_splits, int rows,
+                 int d, int out_dtype, void* stream) {
+  if (!O_part || !LSE_part || !O) return FA_ERR_NULL_PTR;
+  if (num_splits < 1 || rows < 1 || d < 1 || d > 512) return FA_ERR_BAD_SHAPE;
+  if ((long long)num_splits * rows > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  if (out_dtype != FA_BF16 && out_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+  if (!aligned4(O_part) || !aligned4(LSE_part) || !aligned4(O) || (LSE && !aligned4(LSE))) return FA_ERR_ALIGNMENT;
+  return status_of(fa::launch_lse_merge(O_part, LSE_part, O, LSE, num_splits, rows, d, out_dtype == FA_FP32, stream));
+}
+
+}  // extern "C"

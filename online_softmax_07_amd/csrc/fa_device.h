@@ -1,0 +1,59 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types, MFMA
+// wrappers, base-2 transcendentals and lane exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;   // log2(e): e^x = 2^(x * log2 e)
+constexpr float kLn2 = 0.6931471805599453f;     // ln(2):   ln x = log2(x) * ln 2
+constexpr float kNegInf = -__builtin_inff();
+
+// 2^x and log2(x) on the hardware transcendental unit (v_exp_f32 / v_log_f32).
+// exp2(-inf) = 0, which the masked scores rely on.
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// D(32x32 f32) += A(32x16 bf16) * B(16x32 bf16).  Lane l holds A row (l % 32) and B
+// column (l % 32), each with 8 consecutive k of the k-group (l / 32); D element
+// (i, j) sits in lane j + 32 * ((i / 4) % 2), register (i % 4) + 4 * (i / 8).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds A row (l % 16) and B
+// column (l % 16) with 8 k of the k-group (l / 16); D element (i, j) sits in lane
+// j + 16 * (i / 4), register i % 4.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane (l ^ mask) of the 64-lane wave.
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+// Pack halves: result = (hi16 of b or lo16 of b) << 16 | (same half of a).
+// Used to transpose 4x(8 bf16) row chunks into 8x(4 bf16) column chunks.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 v) {
+  return __builtin_convertvector(v, bf16x8);
+}
+
+}  // namespace fa

@@ -1,0 +1,234 @@
+"""Python binding of libfa_mi355x.so (include/fa.h) through ctypes.
+
+Argument marshalling only: the functions below check that the torch tensors they are
+given match the shapes, dtypes and device the C call will assume (the C ABI sees only
+raw pointers and cannot check buffer sizes), allocate outputs when none are passed,
+and call the library on the current HIP stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback path.  If the library is missing it is
+built once (hipcc); if that fails, or the library cannot be loaded, an error is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import sys
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_ALIGNMENT, FA_ERR_HIP = range(7)
+FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
+
+EXPORTED = ("fa_fwd", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+            "fa_lse_merge", "fa_status_string", "fa_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib() -> ctypes.CDLL:
+    """Load (building first only if nothing is built) and declare the C ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build(verbose=False)
+    elif _build.is_stale():
+        sys.stderr.write(f"warning: {_build.LIB} is older than its sources; "
+                         "run `python -m online_softmax_07_amd.build`\n")
+    L = ctypes.CDLL(_build.LIB)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_decode_num_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_decode_num_splits.restype = i
+    L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.fa_decode_workspace_bytes.restype = sz
+    L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, i, vp, sz, i, vp]
+    L.fa_decode_splitkv.restype = i
+    L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    L.fa_lse_merge.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_version.argtypes = []
+    L.fa_version.restype = i
+    _lib = L
+    return L
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_dev(device, **tensors):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _need(t.is_cuda, f"{name} must be a GPU tensor")
+        _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _raise(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# fa_fwd
+# ---------------------------------------------------------------------------
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, *, causal: bool = False, scale: Optional[float] = None,
+           out_dtype: Optional[torch.dtype] = None, want_lse: bool = True, stream=None):
+    """O, LSE = attention(Q, K, V).  q [B,H_q,N_q,d]; k, v [B,H_kv,N_k,d]; bf16 or fp32.
+    bf16 inputs give bf16 O unless ``out_dtype=torch.float32`` (or an fp32 ``o``)."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_k, _ = k.shape
+    _need(k.shape == (B, H_kv, N_k, d) and v.shape == k.shape, "k/v shape mismatch")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    if q.dtype == torch.float32:
+        dtype, odt = FA_FP32, torch.float32
+        _need(out_dtype in (None, torch.float32), "fp32 inputs give fp32 output")
+    elif q.dtype == torch.bfloat16:
+        odt = out_dtype or (o.dtype if o is not None else torch.bfloat16)
+        _need(odt in (torch.bfloat16, torch.float32), "bf16 inputs give bf16 or fp32 output")
+        dtype = FA_BF16 if odt == torch.bfloat16 else FA_BF16_IN_FP32_OUT
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if o is None:
+        o = torch.empty((B, H_q, N_q, d), dtype=odt, device=q.device)
+    _need(o.shape == (B, H_q, N_q, d) and o.dtype == odt, "o has the wrong shape or dtype")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (B, H_q, N_q) and lse.dtype == torch.float32, "lse must be fp32 [B,H_q,N_q]")
+    _check_dev(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H_q, H_kv, N_q, N_k, d,
+                      float(scale), int(bool(causal)), dtype, _stream(stream, q.device))
+    _raise(st, "fa_fwd")
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def fa_decode_num_splits(B, H_q, H_kv, T, N_k, d) -> int:
+    return int(lib().fa_decode_num_splits(B, H_q, H_kv, T, N_k, d))
+
+
+def fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits))
+
+
+def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, *, causal: bool = True,
+                      scale: Optional[float] = None, num_splits: int = 0,
+                      block_table: Optional[torch.Tensor] = None, n_k: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      want_lse: bool = True, check_table: bool = True, stream=None):
+    """Split-KV decode.  q [B,H_q,T,d] bf16.  Contiguous: k, v [B,H_kv,N_k,d].  Paged:
+    k, v pools [num_pages,page_size,H_kv,d] with block_table [B,pages_per_seq] int32 and
+    ``n_k`` tokens per sequence (default pages_per_seq*page_size).  With ``check_table``
+    the table entries are checked to lie inside the pool (one device reduction)."""
+    _need(q.dim() == 4 and q.dtype == torch.bfloat16, "q must be bf16 [B,H_q,T,d]")
+    B, H_q, T, d = q.shape
+    _need(k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and k.shape == v.shape and k.dim() == 4,
+          "k, v must be bf16 4-D tensors of the same shape")
+    if block_table is None:
+        _, H_kv, N_k, _ = k.shape
+        _need(k.shape == (B, H_kv, N_k, d), "contiguous k/v must be [B,H_kv,N_k,d]")
+        page_size = pages_per_seq = 0
+        _need(n_k in (None, N_k), "n_k must equal k.shape[2] for a contiguous cache")
+    else:
+        num_pages, page_size, H_kv, dk = k.shape
+        _need(dk == d, "pool head dimension must match q")
+        _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+              "block_table must be int32 [B, pages_per_seq]")
+        pages_per_seq = block_table.shape[1]
+        N_k = pages_per_seq * page_size if n_k is None else int(n_k)
+        _need(1 <= N_k <= pages_per_seq * page_size, "n_k exceeds the block table")
+        _check_dev(q.device, block_table=block_table)
+        if check_table:
+            lo, hi = int(block_table.min()), int(block_table.max())
+            _need(0 <= lo and hi < num_pages, f"block_table entries must lie in [0, {num_pages})")
+    odt = out_dtype or (o.dtype if o is not None else torch.bfloat16)
+    _need(odt in (torch.bfloat16, torch.float32), "output must be bf16 or fp32")
+    dtype = FA_BF16 if odt == torch.bfloat16 else FA_BF16_IN_FP32_OUT
+    if o is None:
+        o = torch.empty((B, H_q, T, d), dtype=odt, device=q.device)
+    _need(o.shape == (B, H_q, T, d) and o.dtype == odt, "o has the wrong shape or dtype")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (B, H_q, T) and lse.dtype == torch.float32, "lse must be fp32 [B,H_q,T]")
+    need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace.numel() * workspace.element_size() >= need, "workspace too small")
+    _check_dev(q.device, q=q, k=k, v=v, o=o, lse=lse, workspace=workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H_q, H_kv, T, N_k, d,
+                                 float(scale), int(bool(causal)), int(num_splits), _ptr(block_table),
+                                 int(page_size), int(pages_per_seq), _ptr(workspace), ws_bytes, dtype,
+                                 _stream(stream, q.device))
+    _raise(st, "fa_decode_splitkv")
+    return o, lse
+
+
+def fa_lse_merge(o_part: torch.Tensor, lse_part: torch.Tensor, o: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, *, out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """o_part [ns, rows, d] fp32, lse_part [ns, rows] fp32 -> o [rows, d], lse [rows]."""
+    _need(o_part.dim() == 3 and o_part.dtype == torch.float32, "o_part must be fp32 [ns, rows, d]")
+    ns, rows, d = o_part.shape
+    _need(lse_part.shape == (ns, rows) and lse_part.dtype == torch.float32, "lse_part must be fp32 [ns, rows]")
+    odt = o.dtype if o is not None else out_dtype
+    _need(odt in (torch.bfloat16, torch.float32), "output must be bf16 or fp32")
+    if o is None:
+        o = torch.empty((rows, d), dtype=odt, device=o_part.device)
+    _need(o.shape == (rows, d), "o must be [rows, d]")
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
+    _need(lse.shape == (rows,) and lse.dtype == torch.float32, "lse must be fp32 [rows]")
+    _check_dev(o_part.device, o_part=o_part, lse_part=lse_part, o=o, lse=lse)
+    st = lib().fa_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(o), _ptr(lse), ns, rows, d,
+                            FA_BF16 if odt == torch.bfloat16 else FA_FP32, _stream(stream, o_part.device))
+    _raise(st, "fa_lse_merge")
+    return o, lse

@@ -1,0 +1,142 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/fa.h
+declares, and rejects every invalid call with the documented status before any HIP
+call (so these run on a CPU-only host).  No call here ever passes validation: pointers
+are fake, and each case breaks at least one rule."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from online_softmax_07_amd import fa
+from online_softmax_07_amd import build as fabuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000  # a fake, 16-byte aligned "device pointer"; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("fa_fwd", "fa_decode_splitkv", "fa_lse_merge"):
+        assert required in names
+    assert set(names) == set(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_build_is_current():
+    assert not fabuild.is_stale(), "library is older than its sources: rebuild"
+
+
+def test_version_and_status_strings():
+    L = fa.lib()
+    assert L.fa_version() == 100
+    for s in range(7):
+        assert fa.fa_status_string(s).startswith(
+            ["FA_OK", "FA_ERR_NULL_PTR", "FA_ERR_BAD_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
+             "FA_ERR_ALIGNMENT", "FA_ERR_HIP"][s])
+    assert fa.fa_status_string(99) == "unknown fa_status"
+
+
+def fwd(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H_q=2, H_kv=1, N_q=8, N_k=8, d=64, scale=0.125, causal=0,
+             dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H_q"], a["H_kv"], a["N_q"],
+                           a["N_k"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(K=None), fa.FA_ERR_NULL_PTR), (dict(V=None), fa.FA_ERR_NULL_PTR),
+    (dict(O=None), fa.FA_ERR_NULL_PTR),
+    (dict(B=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=0), fa.FA_ERR_BAD_SHAPE), (dict(H_kv=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-3), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(H_q=3, H_kv=2), fa.FA_ERR_BAD_SHAPE), (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=float("inf")), fa.FA_ERR_BAD_SHAPE), (dict(causal=2), fa.FA_ERR_BAD_SHAPE),
+    (dict(B=70000, H_q=70000, H_kv=70000), fa.FA_ERR_BAD_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED), (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(Q=P + 8), fa.FA_ERR_ALIGNMENT), (dict(O=P + 2), fa.FA_ERR_ALIGNMENT), (dict(LSE=P + 2), fa.FA_ERR_ALIGNMENT),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+def dec(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H_q=4, H_kv=2, T=1, N_k=100, d=128, scale=0.1, causal=1, ns=4,
+             bt=None, ps=0, pps=0, ws=P, wsb=1 << 20, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_decode_splitkv(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H_q"], a["H_kv"],
+                                      a["T"], a["N_k"], a["d"], a["scale"], a["causal"], a["ns"], a["bt"],
+                                      a["ps"], a["pps"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR),
+    (dict(T=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=5), fa.FA_ERR_BAD_SHAPE),
+    (dict(ns=-1), fa.FA_ERR_BAD_SHAPE), (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE), (dict(causal=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(bt=P, ps=0, pps=7), fa.FA_ERR_BAD_SHAPE), (dict(bt=P, ps=16, pps=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(bt=P, ps=16, pps=6), fa.FA_ERR_BAD_SHAPE),   # 6 * 16 < 100 keys
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=300, H_q=300, H_kv=300), fa.FA_ERR_UNSUPPORTED),   # B*H_kv beyond the grid's y range
+    (dict(K=P + 4), fa.FA_ERR_ALIGNMENT), (dict(bt=P + 2, ps=16, pps=7), fa.FA_ERR_ALIGNMENT),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE), (dict(ns=0, N_k=100000, wsb=10), fa.FA_ERR_WORKSPACE),
+    (dict(ws=P + 4), fa.FA_ERR_ALIGNMENT),
+])
+def test_decode_rejects(kw, status):
+    assert dec(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Op=None), fa.FA_ERR_NULL_PTR), (dict(Lp=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR),
+    (dict(ns=0), fa.FA_ERR_BAD_SHAPE), (dict(rows=0), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(d=513), fa.FA_ERR_BAD_SHAPE), (dict(dtype=fa.FA_BF16_IN_FP32_OUT), fa.FA_ERR_UNSUPPORTED),
+    (dict(Op=P + 1), fa.FA_ERR_ALIGNMENT),
+])
+def test_merge_rejects(kw, status):
+    a = dict(Op=P, Lp=P, O=P, L=P, ns=4, rows=8, d=128, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    assert fa.lib().fa_lse_merge(a["Op"], a["Lp"], a["O"], a["L"], a["ns"], a["rows"], a["d"], a["dtype"],
+                                 a["stream"]) == status
+
+
+def test_workspace_and_split_sizes():
+    # one split needs no workspace
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 1) == 0
+    # ns partial rows of d fp32 plus ns lse values, each part rounded to 256 bytes
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == 8 * 32 * 128 * 4 + 1024
+    assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == 4 * 512 * 128 * 4 + 4 * 512 * 4
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 0
+    # the automatic split count aims at one wave of 2 workgroups on each of 256 CUs
+    assert fa.fa_decode_num_splits(1, 32, 8, 1, 131072, 128) == 64
+    assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 8
+    assert fa.fa_decode_num_splits(256, 32, 8, 1, 4096, 128) == 1
+    assert fa.fa_decode_num_splits(1, 32, 8, 1, 300, 128) == 2  # never more splits than 256-key pieces
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 0) == fa.fa_decode_workspace_bytes(
+        1, 32, 8, 1, 131072, 128, 64)
+
+
+def test_binding_refuses_host_tensors():
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q, o=torch.zeros_like(q), lse=torch.zeros(1, 1, 4), stream=0)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q[:, :, :3], q)

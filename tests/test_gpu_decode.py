@@ -1,0 +1,146 @@
+"""fa_decode_splitkv and fa_lse_merge on the GPU against the fp64 oracle, through the
+C ABI.  The full-size decode workloads are small enough in rows that every output row
+is compared, for every split count swept."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.fa_oracle as orc
+from online_softmax_07_amd import fa, workloads
+from parity import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host(t):
+    return t.float().numpy()
+
+
+def run_decode(w, ns, out_dtype=torch.bfloat16, q=None, k=None, v=None, bt=None):
+    q = w.q.to(DEV) if q is None else q
+    k = w.k.to(DEV) if k is None else k
+    v = w.v.to(DEV) if v is None else v
+    if w.block_table is not None and bt is None:
+        bt = w.block_table.to(DEV)
+    o = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_decode_splitkv(q, k, v, o, lse, causal=w.causal, scale=w.scale, num_splits=ns, block_table=bt,
+                         n_k=w.n_k)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_of(w):
+    bt = None if w.block_table is None else w.block_table.numpy()
+    return orc.decode(host(w.q), host(w.k), host(w.v), w.scale, w.causal, block_table=bt,
+                      page_size=w.page_size or None, n_k=w.n_k)
+
+
+@pytest.fixture(scope="module")
+def c4():
+    w = workloads.decode_splitkv_128k()
+    say(w.name, "oracle")
+    return w, oracle_of(w), (w.q.to(DEV), w.k.to(DEV), w.v.to(DEV))
+
+
+@pytest.mark.parametrize("ns", [1, 8, 16, 32, 64, 0])
+def test_decode_splitkv_128k(c4, ns):
+    w, (O, L), (q, k, v) = c4
+    say(w.name, "num_splits", ns)
+    o, lse = run_decode(w, ns, q=q, k=k, v=v)
+    check_o(o, O, "bf16")
+    check_lse(lse, L)
+    o32, lse32 = run_decode(w, ns, torch.float32, q=q, k=k, v=v)
+    check_o(o32, O, "fp32out")
+    check_lse(lse32, L)
+
+
+@pytest.fixture(scope="module")
+def c5():
+    w = workloads.decode_paged_b64()
+    say(w.name, "oracle")
+    return w, oracle_of(w), (w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), w.block_table.to(DEV))
+
+
+@pytest.mark.parametrize("ns", [1, 2, 4, 8, 0])
+def test_decode_paged_b64(c5, ns):
+    w, (O, L), (q, k, v, bt) = c5
+    say(w.name, "num_splits", ns)
+    o, lse = run_decode(w, ns, q=q, k=k, v=v, bt=bt)
+    check_o(o, O, "bf16")
+    check_lse(lse, L)
+    o32, lse32 = run_decode(w, ns, torch.float32, q=q, k=k, v=v, bt=bt)
+    check_o(o32, O, "fp32out")
+    check_lse(lse32, L)
+
+
+# B, H_q, H_kv, T, N_k, d, causal, page_size, ns
+SMALL = [
+    (1, 4, 1, 1, 64, 128, True, 0, 1),
+    (2, 8, 2, 1, 1000, 128, True, 0, 3),
+    (1, 4, 4, 4, 333, 128, True, 0, 2),      # T > 1, bottom-right mask, g = 1
+    (2, 8, 2, 3, 77, 64, True, 0, 8),        # splits beyond the keys are empty
+    (1, 16, 2, 3, 500, 128, True, 0, 4),     # 24 stacked rows: two row chunks
+    (1, 32, 1, 1, 200, 64, False, 0, 2),     # 32 heads in one group
+    (3, 8, 1, 2, 129, 128, False, 0, 5),
+    (1, 4, 2, 5, 3, 128, True, 0, 1),        # T > N_k: rows that see no key
+    (2, 8, 1, 1, 300, 128, True, 16, 4),     # paged
+    (2, 4, 2, 2, 101, 128, True, 5, 3),      # odd page size, ragged last page
+    (1, 8, 8, 1, 1024, 64, True, 64, 0),
+    (4, 8, 1, 1, 8192, 128, True, 16, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_decode_small(case):
+    B, Hq, Hkv, T, Nk, d, causal, ps, ns = case
+    w = workloads.decode(B, Hq, Hkv, T, Nk, d, seed=sum(case), causal=causal, page_size=ps,
+                         num_pages=None if ps == 0 else B * (-(-Nk // ps)) + 3)
+    say("decode", case)
+    O, L = oracle_of(w)
+    o, lse = run_decode(w, ns)
+    check_o(o, O, "bf16")
+    check_lse(lse, L)
+    o32, lse32 = run_decode(w, ns, torch.float32)
+    check_o(o32, O, "fp32out")
+    check_lse(lse32, L)
+
+
+# ---------------------------------------------------------------------------
+# fa_lse_merge on its own
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bounds", [[(0, 50)], [(0, 10), (10, 50)], [(0, 0), (0, 7), (7, 7), (7, 50)],
+                                    [(i, i + 1) for i in range(50)] + [(50, 50)] * 20])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge(bounds, out_dtype):
+    rng = np.random.default_rng(len(bounds))
+    B, Hq, Hkv, T, Nk, d = 2, 4, 2, 3, 50, 128
+    Q = rng.standard_normal((B, Hq, T, d))
+    K = rng.standard_normal((B, Hkv, Nk, d)) * 1.5
+    V = rng.standard_normal((B, Hkv, Nk, d))
+    Op, Lp = orc.split_partials(Q, K, V, 0.1, True, bounds)
+    O, L = orc.attention(Q, K, V, 0.1, True)
+    ns = len(bounds)
+    rows = B * Hq * T
+    op = torch.from_numpy(Op.reshape(ns, rows, d).astype(np.float32)).to(DEV)
+    lp = torch.from_numpy(Lp.reshape(ns, rows).astype(np.float32)).to(DEV)
+    say("merge", ns, out_dtype)
+    o, lse = fa.fa_lse_merge(op, lp, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    check_o(o.reshape(B, Hq, T, d), O, "bf16" if out_dtype == torch.bfloat16 else "fp32out")
+    check_lse(lse.reshape(B, Hq, T), L, tol=1e-5)
+
+
+def test_lse_merge_all_empty():
+    op = torch.zeros(3, 4, 64, device=DEV)
+    lp = torch.full((3, 4), float("-inf"), device=DEV)
+    o, lse = fa.fa_lse_merge(op, lp, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
