@@ -1,24 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu]
 
-One step is one fa_fwd call on the prefill workload B=4, H_q=H_kv=16, N=4096, d=128,
-causal (bottom-right), bf16 in / bf16 O + fp32 LSE out, inputs resident in HBM.  The
+Default step: one fa_fwd call on the prefill workload B=4, H_q=H_kv=16, N=4096, d=128,
+causal (bottom-right), bf16 in, bf16 O and fp32 LSE out, inputs resident in HBM.  The
 headline ``value`` is its attention throughput in TFLOP/s (4 N^2 d per head, halved for
-causal).  ``roofline`` prices the prefill kernel's average launch (HIP events on the
-launch stream) against the dense bf16 MFMA peak.  ``breakdown`` adds the other prefill
-variants, the long causal prefill, and the two decode workloads (HBM GB/s against the
-HBM peak, with L2 and the Infinity Cache flushed between timed calls).
-``cpu_baseline`` times the fp64 oracle on a bounded sample of the headline workload.
-Prints exactly one JSON line.
+causal).  ``roofline`` prices the dominant kernel's average launch (HIP events recorded on
+the stream the library launches on) against the dense bf16 MFMA peak (prefill) or the
+HBM peak (decode), with ``traffic`` taken from the committed rocprofv3 counter summary
+when it was measured on the current kernel source.  ``breakdown`` adds the other
+prefill variants, the long causal prefill and the two decode workloads (decode timed
+with L2 and the Infinity Cache flushed before every call).  ``cpu_baseline`` times the
+fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
+
+``--workload`` makes another workload the timed one (for profiling); ``--calib-copy``
+adds a plain 1 GiB device copy (torch's copy kernel), the reference that scales the
+HBM byte counters.
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import statistics
 import sys
@@ -26,6 +30,12 @@ import time
 
 METRIC = "attention TFLOP/s + % MFMA peak (prefill); HBM GB/s + % peak (decode), 1 GPU"
 HERE = os.path.dirname(os.path.abspath(__file__))
+PREFILL = {
+    "prefill_d128_causal": (128, True), "prefill_d128_full": (128, False),
+    "prefill_d64_causal": (64, True), "prefill_d64_full": (64, False),
+}
+DECODE = ("decode_splitkv_128k", "decode_paged_b64")
+WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + DECODE
 
 
 def parse():
@@ -33,10 +43,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--no-extra", action="store_true", help="headline workload only (for profiling)")
+    p.add_argument("--workload", default="prefill_d128_causal", choices=WORKLOADS)
+    p.add_argument("--num-splits", type=int, default=0, help="decode split count for --workload (0 = auto)")
+    p.add_argument("--no-extra", action="store_true", help="time the --workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--only", default=None, help="run one breakdown entry as the only timed work")
-    p.add_argument("--out", default=None, help="also write the JSON to this file")
+    p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy (counter calibration)")
+    p.add_argument("--out", default=None, help="also write the JSON line to this file")
     return p.parse_args()
 
 
@@ -44,13 +56,13 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library is single-GPU: run bench.py with --gpus 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
     import torch
     sys.path.insert(0, HERE)
-    from online_softmax_07_amd import fa, roofline as rl, workloads
+    from online_softmax_07_amd import build as fabuild, fa, roofline as rl, workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -58,7 +70,8 @@ def main():
 
     def timed(fn, steps, warmup, pre=None):
         """Per-call durations (ms) from HIP events recorded on the launch stream, and the
-        total bracketed time of the K calls."""
+        bracketed total of the K calls (pre(), e.g. a cache flush, sits outside each call's
+        bracket but inside the total)."""
         for _ in range(warmup):
             if pre:
                 pre()
@@ -78,10 +91,17 @@ def main():
             en[i].record(stream)
         t1.record(stream)
         torch.cuda.synchronize()
-        per = [a.elapsed_time(b) for a, b in zip(st, en)]
-        return t0.elapsed_time(t1), per
+        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in zip(st, en)]
 
-    # ---- prefill workloads ----
+    def make(name):
+        if name in PREFILL:
+            return workloads.prefill_4x16x4096(*PREFILL[name])
+        if name == "long_prefill_8192":
+            return workloads.long_prefill_8192()
+        if name == "decode_splitkv_128k":
+            return workloads.decode_splitkv_128k()
+        return workloads.decode_paged_b64()
+
     def prefill_case(w):
         q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
         o = torch.empty_like(q)
@@ -93,19 +113,58 @@ def main():
             fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
         return fn, flops, (q, k, v, o, lse)
 
-    # ---- headline: prefill B=4 H=16 N=4096 d=128 causal ----
-    head_w = workloads.prefill_4x16x4096(128, True)
-    fn, flops, bufs = prefill_case(head_w)
-    total_ms, per = timed(fn, args.steps, args.warmup)
-    ms_per_step = total_ms / args.steps
-    avg_launch_ms = statistics.mean(per)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    s = head_w.shape
+    def decode_case(w, ns):
+        q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+        bt = None if w.block_table is None else w.block_table.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        sh = w.shape
+        pps = 0 if bt is None else bt.shape[1]
+        nbytes = rl.decode_bytes(sh["B"], sh["H_q"], sh["H_kv"], sh["T"], sh["N_k"], sh["d"], pps)
+        wsb = fa.fa_decode_workspace_bytes(sh["B"], sh["H_q"], sh["H_kv"], sh["T"], sh["N_k"], sh["d"], ns)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        if bt is not None:   # validate the table once, outside any timing
+            assert 0 <= int(bt.min()) and int(bt.max()) < w.k.shape[0]
+
+        def fn():
+            fa.fa_decode_splitkv(q, k, v, o, lse, causal=w.causal, scale=w.scale, num_splits=ns,
+                                 block_table=bt, n_k=w.n_k, workspace=ws, check_table=False, stream=stream)
+        return fn, nbytes, (q, k, v, bt, o, lse, ws)
+
+    flush = None
+
+    def flush_caches():
+        flush.fill_(1)
+
+    # ---- the timed workload ----
+    head = args.workload
+    w = make(head)
+    s = w.shape
+    if head in DECODE:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB: evicts L2 and MALL
+        fn, nbytes, bufs = decode_case(w, args.num_splits)
+        total_ms, per = timed(fn, args.steps, args.warmup, pre=flush_caches)
+        avg = statistics.mean(per)
+        ms_per_step = avg   # the flush between calls is not part of the step
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit, bound, peak, achieved = "GB/s", "hbm", rl.PEAK_HBM_GBPS, nbytes / (avg * 1e-3) / 1e9
+        kernel = "fa::decode_split_kernel + fa::lse_merge_kernel"
+        extra_cfg = {"T": s["T"], "num_splits": args.num_splits or fa.fa_decode_num_splits(
+            s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"]), "bytes_per_step": nbytes,
+            "paged": w.block_table is not None}
+    else:
+        fn, flops, bufs = prefill_case(w)
+        total_ms, per = timed(fn, args.steps, args.warmup)
+        avg = statistics.mean(per)
+        ms_per_step = total_ms / args.steps
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit, bound, peak, achieved = "TFLOP/s", "mfma", rl.PEAK_BF16_MFMA_TFLOPS, flops / (avg * 1e-3) / 1e12
+        kernel = f"fa::fwd_bf16_kernel<{s['d']}, {64 if s['d'] == 128 else 128}, {str(w.causal).lower()}, bf16>"
+        extra_cfg = {"N_q": s["N_q"], "N_k": s["N_k"], "causal": w.causal, "flops_per_step": flops}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -114,106 +173,111 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: iid N(0,1) rounded to bf16, seed 201",
-        "config": {"workload": head_w.name, "B": s["B"], "H_q": s["H_q"], "H_kv": s["H_kv"],
-                   "N_q": s["N_q"], "N_k": s["N_k"], "d": s["d"], "causal": True,
-                   "flops_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": rl.PEAK_BF16_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / rl.PEAK_BF16_MFMA_TFLOPS, 4),
-                     "traffic": None, "kernel": "fa::fwd_bf16_kernel<128, 64, true, bf16>",
-                     "avg_launch_us": round(avg_launch_ms * 1e3, 2)},
+        "data": "synthetic: iid N(0,1) rounded to bf16 (seeded)",
+        "config": {"workload": w.name, "B": s["B"], "H_q": s["H_q"], "H_kv": s["H_kv"], "d": s["d"], **extra_cfg},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel,
+                     "avg_launch_us": round(avg * 1e3, 2)},
     }
+    traffic = load_traffic(w.name, fabuild)
+    if traffic is not None:
+        result["roofline"]["traffic"] = traffic
     del bufs
 
     # ---- breakdown ----
-    breakdown = {}
     if not args.no_extra:
-        for d, causal in [(64, False), (64, True), (128, False)]:
-            w = workloads.prefill_4x16x4096(d, causal)
-            fn, fl, bufs = prefill_case(w)
+        breakdown = {}
+        for name in WORKLOADS:
+            if name == head or name in DECODE:
+                continue
+            ww = make(name)
+            fn, fl, bufs = prefill_case(ww)
             _, per = timed(fn, max(10, args.steps // 2), 3)
             med = statistics.median(per)
-            breakdown[w.name] = {"us": round(med * 1e3, 2), "TFLOP/s": round(fl / med / 1e9, 2),
-                                 "frac_mfma": round(fl / med / 1e9 / rl.PEAK_BF16_MFMA_TFLOPS, 4)}
+            breakdown[ww.name] = {"us": round(med * 1e3, 2), "TFLOP/s": round(fl / med / 1e9, 2),
+                                  "frac_mfma": round(fl / med / 1e9 / rl.PEAK_BF16_MFMA_TFLOPS, 4)}
             del bufs
-        w = workloads.long_prefill_8192()
-        fn, fl, bufs = prefill_case(w)
-        _, per = timed(fn, max(10, args.steps // 2), 3)
-        med = statistics.median(per)
-        breakdown[w.name] = {"us": round(med * 1e3, 2), "TFLOP/s": round(fl / med / 1e9, 2),
-                             "frac_mfma": round(fl / med / 1e9 / rl.PEAK_BF16_MFMA_TFLOPS, 4)}
-        del bufs
-
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB: evicts L2 and MALL
-
-        def pre():
-            flush.fill_(1)
-
-        for w in (workloads.decode_splitkv_128k(), workloads.decode_paged_b64()):
-            q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
-            bt = None if w.block_table is None else w.block_table.to(dev)
-            o = torch.empty_like(q)
-            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-            sh = w.shape
-            pps = 0 if bt is None else bt.shape[1]
-            nbytes = rl.decode_bytes(sh["B"], sh["H_q"], sh["H_kv"], sh["T"], sh["N_k"], sh["d"], pps)
-            entry = {"bytes": nbytes, "by_num_splits": {}}
-            best = None
-            for ns in list(w.num_splits) + [0]:
-                wsb = fa.fa_decode_workspace_bytes(sh["B"], sh["H_q"], sh["H_kv"], sh["T"], sh["N_k"], sh["d"], ns)
-                ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-
-                def fn(ns=ns, ws=ws):
-                    fa.fa_decode_splitkv(q, k, v, o, lse, causal=w.causal, scale=w.scale, num_splits=ns,
-                                         block_table=bt, n_k=w.n_k, workspace=ws, check_table=False,
-                                         stream=stream)
-                _, per = timed(fn, 30, 3, pre=pre)
+        if flush is None:
+            flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for name in DECODE:
+            ww = make(name)
+            entry, best = {"by_num_splits": {}}, None
+            for ns in list(ww.num_splits) + [0]:
+                fn, nbytes, bufs = decode_case(ww, ns)
+                _, per = timed(fn, 30, 3, pre=flush_caches)
                 med = statistics.median(per)
                 gbs = nbytes / (med * 1e-3) / 1e9
                 key = "auto" if ns == 0 else str(ns)
                 entry["by_num_splits"][key] = {"us": round(med * 1e3, 2), "min_us": round(min(per) * 1e3, 2),
-                                               "GB/s": round(gbs, 1),
-                                               "frac_hbm": round(gbs / rl.PEAK_HBM_GBPS, 4)}
+                                               "GB/s": round(gbs, 1), "frac_hbm": round(gbs / rl.PEAK_HBM_GBPS, 4)}
                 if best is None or gbs > best[1]:
                     best = (key, gbs)
+                del bufs
+            entry["bytes"] = nbytes
             entry["best"] = {"num_splits": best[0], "GB/s": round(best[1], 1),
                              "frac_hbm": round(best[1] / rl.PEAK_HBM_GBPS, 4)}
-            breakdown[w.name] = entry
-            del q, k, v, bt, o, lse
-        del flush
+            breakdown[ww.name] = entry
         result["breakdown"] = breakdown
+    del flush
 
-    # ---- CPU baseline: the fp64 oracle on a bounded sample of the headline workload ----
-    if not args.no_cpu:
-        import oracle.fa_oracle as orc
-        from threadpoolctl import threadpool_info
-        q = head_w.q.float().numpy()
-        k = head_w.k.float().numpy()
-        v = head_w.v.float().numpy()
-        heads = 0
-        t0 = time.perf_counter()
-        B, H = q.shape[:2]
-        for bh in range(B * H):
-            b, h = divmod(bh, H)
-            orc.attention_head(q[b, h], k[b, h], v[b, h], head_w.scale, True)
-            heads += 1
-            if time.perf_counter() - t0 > 10.0:
-                break
-        el = time.perf_counter() - t0
-        fl = rl.prefill_flops(1, heads, s["N_q"], s["N_k"], s["d"], True)
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        result["cpu_baseline"] = {
-            "value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
-            "cores": min(threads, len(os.sched_getaffinity(0))), "kind": "oracle",
-            "sample": f"fp64 numpy oracle on {heads} of {B * H} (batch, head) pairs, all 4096 rows each, "
-                      f"{el:.1f} s; same FLOP convention",
-        }
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(3)
+        torch.cuda.synchronize()
+        _, per = timed(lambda: b.copy_(a), 5, 2)
+        result["calib_copy"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                                "us": round(statistics.median(per) * 1e3, 2)}
+        del a, b
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the timed workload ----
+    if not args.no_cpu and head not in DECODE:
+        result["cpu_baseline"] = cpu_baseline(w, rl)
 
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:
         with open(args.out, "w") as f:
             f.write(line + "\n")
+
+
+def cpu_baseline(w, rl):
+    """The fp64 numpy oracle, untuned, on whole (batch, head) pairs of the workload until
+    about 10 s of CPU time have been spent; reported in the metric's unit."""
+    import oracle.fa_oracle as orc
+    from threadpoolctl import threadpool_info
+    q, k, v = (t.float().numpy() for t in (w.q, w.k, w.v))
+    B, H = q.shape[:2]
+    g = H // k.shape[1]
+    heads = 0
+    t0 = time.perf_counter()
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        orc.attention_head(q[b, h], k[b, h // g], v[b, h // g], w.scale, w.causal)
+        heads += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    el = time.perf_counter() - t0
+    s = w.shape
+    fl = rl.prefill_flops(1, heads, s["N_q"], s["N_k"], s["d"], w.causal)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(threads, len(os.sched_getaffinity(0))), "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {heads} of {B * H} (batch, head) pairs of {w.name}, "
+                      f"all rows each, {el:.1f} s; same FLOP convention"}
+
+
+def load_traffic(workload_name, fabuild):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(HERE, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != fabuild.source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 if __name__ == "__main__":
