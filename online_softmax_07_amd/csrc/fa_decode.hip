@@ -160,11 +160,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-        s[kb][r] = p;
-        psum += p;
+        s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+        psum += s[kb][r];
       }
     l_run = l_run * alpha + psum;
+    // P^T operands (bf16, RNE) for the two 32-key steps
+    bf16x8 pf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      pf[u] = to_bf16x8(f32x8{s[2 * u][0], s[2 * u][1], s[2 * u][2], s[2 * u][3],
+                              s[2 * u + 1][0], s[2 * u + 1][1], s[2 * u + 1][2], s[2 * u + 1][3]});
     m_run = m_new;
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) o[cb] *= alpha;
@@ -198,12 +203,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     // ---- O^T += V^T P^T (two k-steps of 32 keys) ----
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const bf16x8 pf = to_bf16x8(f32x8{s[2 * u][0], s[2 * u][1], s[2 * u][2], s[2 * u][3],
-                                        s[2 * u + 1][0], s[2 * u + 1][1], s[2 * u + 1][2], s[2 * u + 1][3]});
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (cb * 16 + l16) * VPITCH + 32 * u + 8 * g4);
-        o[cb] = mfma16x16x32(vf, pf, o[cb]);
+        o[cb] = mfma16x16x32(vf, pf[u], o[cb]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

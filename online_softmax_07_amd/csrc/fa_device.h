@@ -56,4 +56,61 @@ __device__ __forceinline__ bf16x8 to_bf16x8(f32x8 v) {
   return __builtin_convertvector(v, bf16x8);
 }
 
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// supplies the address of 4 consecutive 16-bit values; result lane i receives, in slot
+// s, value (i % 4) of lane (4 s + i / 4)'s four.  Two such reads fill one 8-element
+// MFMA operand whose k index runs across the rows the source lanes point at.
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<__bf16*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(s16x4 lo, s16x4 hi) {
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// True in every lane if `pred` holds in any active lane (wave-uniform).
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the eight bf16 values of an MFMA operand, accumulated in fp32 (v_dot2c_f32_bf16
+// against (1, 1)).  Summing the rounded values the PV product uses keeps numerator and
+// denominator of O = sum p V / sum p consistent.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+
+// Raw buffer access (gfx9 family descriptor).  Loads at byte offsets >= `bytes` return
+// zero, which is how tiles running past the end of a sequence are zero-filled without
+// any per-element test.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0));
+}
+
+// Bytes from element `start` to the end of a range of `n` rows of `row_bytes`, clamped to
+// the 32-bit descriptor range.
+__device__ __forceinline__ uint32_t range_bytes(long long rows_left, int row_bytes) {
+  const long long b = rows_left <= 0 ? 0 : rows_left * (long long)row_bytes;
+  return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
+}
+
 }  // namespace fa

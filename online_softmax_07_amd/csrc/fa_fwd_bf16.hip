@@ -11,15 +11,25 @@
 // MI355X mapping:
 //   * 4 waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
 //     32x32x16 bf16 MFMA: K (from LDS) is the A operand, the wave's Q rows (registers,
-//     loaded once) the B operand.  In the accumulator layout each lane then owns ONE query
-//     row (lane % 32) and 16 keys per 32-key block, so the row max is a register reduction
+//     loaded once) the B operand.  In the accumulator layout each lane owns ONE query row
+//     (lane % 32) and 16 keys per 32-key block, so the row max is a register reduction
 //     plus one exchange between the two wave halves, the row sum stays a per-lane partial
-//     until the end, and the rescale factor alpha is a per-lane scalar.
+//     until the end, and the rescale factor is a per-lane scalar.
 //   * O^T = V^T P^T on the same MFMA: P^T comes straight from the score registers
-//     (converted to bf16), V^T is read from an LDS copy of the V tile that was transposed
-//     while it was staged (4 key rows x 8 columns per thread, regrouped with v_perm).
-//   * K/V tiles: coalesced 16-byte global loads into registers one tile ahead, then into
-//     padded (bank-conflict-free for the MFMA reads) LDS tiles.
+//     (converted to bf16); V^T fragments are read from the row-major V tile in LDS with
+//     the transposing LDS read (ds_read_b64_tr_b16), so V is staged exactly like K.
+//   * K/V tiles: coalesced 16-byte raw buffer loads (zero past the end of the sequence)
+//     held in registers one tile ahead, then written to a double-buffered LDS ring; one
+//     barrier per tile.  Row pitches are padded
+//     so the MFMA operand reads (plain for K, transposing for V) are bank-conflict free.
+//   * Independent accumulators are interleaved and operand fragments are read one step
+//     ahead of the MFMA that consumes them.
+//   * The running max is only moved (and l, O rescaled) when a row's tile max exceeds it
+//     by more than 2^8 in the exponent; until then p <= 2^8.  O = acc / l and
+//     LSE = m + ln l are exact for any reference m, so this only skips work (the skip is
+//     wave-uniform).  O is divided by the sum of the same bf16-rounded P the PV product
+//     uses (v_dot2 against (1, 1)), so the rounding of a dominant weight (which need not
+//     be 1 under a lagging max) cancels in O = sum p V / sum p; the LSE uses the fp32 sum.
 //   * Workgroup order: heaviest causal query blocks first, and consecutive blocks of a
 //     head kept on one XCD so the K/V re-reads of the FlashAttention-2 order hit its L2.
 //   * Softmax in base 2: p = 2^(s * scale * log2 e - m), with m kept in the same units.
@@ -30,23 +40,20 @@ namespace fa {
 
 constexpr int kBR = 128;      // query rows per workgroup
 constexpr int kThreads = 256; // 4 waves
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
 
 template <int D, int BC>
 struct FwdTile {
-  static constexpr int KPITCH = D + 8;   // bf16 elements per K row in LDS (16-byte pad)
-  static constexpr int VPITCH = BC + 8;  // bf16 elements per V^T row in LDS
-  static constexpr int CHUNKS = D / 8;   // 16-byte chunks per K/V row
-  static constexpr int KLOADS = BC * CHUNKS / kThreads;  // K chunks per thread per tile
-  static_assert(BC * CHUNKS % kThreads == 0, "K tile must split evenly");
-  static_assert((BC / 4) * CHUNKS == kThreads, "V tile: one 4-row x 8-col unit per thread");
+  static constexpr int KP = D + 8;          // K row pitch (bf16): 16-byte pad -> plain b128 reads conflict free
+  static constexpr int VP = D + 16;         // V row pitch: 32-byte pad -> transposing reads conflict free
+  static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
+  static constexpr int LOADS = BC * CHUNKS / kThreads;  // chunks per thread per tile, for K and for V
+  static constexpr int NKB = BC / 32;       // 32-key blocks per tile
+  static constexpr int NCB = D / 32;        // 32-column blocks of O^T
+  static constexpr int KSTAGE = BC * KP;
+  static constexpr int VSTAGE = BC * VP;
+  static_assert(BC * CHUNKS % kThreads == 0, "tile must split evenly over the threads");
 };
-
-// Position of key k (0 <= k < BC) inside a V^T row in LDS.  Keys are grouped by 16; in a
-// group, key 8a + 4h + b (a, h in {0,1}, b in 0..3) goes to 8h + 4a + b, so the eight keys
-// that one MFMA k-group of P^T holds (see the S^T accumulator layout) are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
-}
 
 template <int D, int BC, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -54,11 +61,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
     float scale_log2, int n_qblocks, int total_wg) {
   using T = FwdTile<D, BC>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BC * T::KPITCH];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * T::VPITCH];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * T::KSTAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2 * T::VSTAGE];
 
   // ---- which (batch, head, query block) this workgroup owns ----
-  int wg = blockIdx.x;
+  const int wg = blockIdx.x;
   int logical = wg;
   if ((total_wg & 7) == 0) logical = (wg & 7) * (total_wg >> 3) + (wg >> 3);  // XCD-contiguous
   const int bh = logical / n_qblocks;
@@ -74,170 +81,192 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
-  const int hh = lane >> 5;  // k-group of the MFMA operands
+  const int hh = lane >> 5;      // k-group of the MFMA operands
+  const int g16 = lane >> 4;     // 16-lane group (transposing reads)
+  const int i16 = lane & 15;
   const int q0 = qb * kBR;
   const int wave_row0 = q0 + wave * 32;
   const int qrow = wave_row0 + l32;
-  const int shift = N_k - N_q;  // bottom-right alignment: row i sees keys j <= i + shift
+  const int shift = N_k - N_q;   // bottom-right alignment: row i sees keys j <= i + shift
 
   // ---- Q block: read once, kept as MFMA B fragments ----
   bf16x8 qf[D / 16];
+  {
+    const int qr = qrow < N_q ? qrow : N_q - 1;  // clamped row; zeroed below
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    if (qrow < N_q) {
-      qf[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qrow * D + 16 * t + 8 * hh);
-    } else {
-      qf[t] = bf16x8{};
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qr * D + 16 * t + 8 * hh);
+      if (qrow >= N_q) qf[t] = bf16x8{};
     }
   }
 
   // ---- which K/V tiles this block visits ----
   int n_tiles = (N_k + BC - 1) / BC;
   if (CAUSAL) {
-    const int last_row = min(q0 + kBR - 1, N_q - 1);
-    const int max_key = last_row + shift;
+    const int max_key = min(q0 + kBR - 1, N_q - 1) + shift;
     n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
   }
   const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;  // causal reach of this wave
+  const int row_lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1; // last key this row sees
 
-  // ---- carries (one query row per lane; l is this lane's partial over its keys) ----
-  float m_run = kNegInf;
-  float l_run = 0.f;
-  f32x16 o[D / 32];
+  // ---- carries ----
+  float m_run = kNegInf;  // reference max (log2 units of the scaled scores)
+  float l_run = 0.f;      // this lane's partial sum of p over its keys (fp32 p: for the LSE)
+  float lb_run = 0.f;     // the same sum over the bf16-rounded p the PV product uses (for O)
+  f32x16 o[T::NCB];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+  for (int cb = 0; cb < T::NCB; ++cb) o[cb] = f32x16{};
 
-  // ---- register staging of the next K/V tile ----
-  u32x4 kreg[T::KLOADS];
-  u32x4 vreg[4];
-  const int v_quad = tid / T::CHUNKS;  // 4 consecutive keys
-  const int v_chunk = tid % T::CHUNKS; // 8 consecutive columns
-
+  // ---- K/V staging: global -> registers -> LDS stage ----
+  // Raw buffer loads with a descriptor that starts at the tile and ends at N_k: rows past
+  // the end of the sequence read as zeros (K: scores that get masked; V: 0 * V = 0).
+  u32x4 kreg[T::LOADS], vreg[T::LOADS];
+  uint32_t goff[T::LOADS];   // byte offset of this thread's chunks inside a tile
+  int loff_k[T::LOADS], loff_v[T::LOADS];  // and their element offsets in an LDS stage
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int c = i * kThreads + tid;
+    const int row = c / T::CHUNKS;
+    const int col = c % T::CHUNKS;
+    goff[i] = (uint32_t)(row * D + col * 8) * 2u;
+    loff_k[i] = row * T::KP + col * 8;
+    loff_v[i] = row * T::VP + col * 8;
+  }
   auto load_tile = [&](int j) {
     const int kbase = j * BC;
+    const uint32_t bytes = range_bytes((long long)N_k - kbase, D * 2);
+    const auto kr = make_rsrc(Kp + (size_t)kbase * D, bytes);
+    const auto vr = make_rsrc(Vp + (size_t)kbase * D, bytes);
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / T::CHUNKS;
-      const int col = c % T::CHUNKS;
-      const int key = kbase + row;
-      kreg[i] = key < N_k ? *reinterpret_cast<const u32x4*>(Kp + (size_t)key * D + col * 8) : u32x4{};
+    for (int i = 0; i < T::LOADS; ++i) {
+      kreg[i] = buffer_load16(kr, goff[i]);
+      vreg[i] = buffer_load16(vr, goff[i]);
     }
+  };
+  auto store_tile = [&](int stage) {
+    __bf16* ks = Ks + stage * T::KSTAGE;
+    __bf16* vs = Vs + stage * T::VSTAGE;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kbase + v_quad * 4 + r;
-      vreg[r] = key < N_k ? *reinterpret_cast<const u32x4*>(Vp + (size_t)key * D + v_chunk * 8) : u32x4{};
+    for (int i = 0; i < T::LOADS; ++i) {
+      *reinterpret_cast<u32x4*>(ks + loff_k[i]) = kreg[i];
+      *reinterpret_cast<u32x4*>(vs + loff_v[i]) = vreg[i];
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c / T::CHUNKS;
-      const int col = c % T::CHUNKS;
-      *reinterpret_cast<u32x4*>(Ks + row * T::KPITCH + col * 8) = kreg[i];
-    }
-    // transpose 4 keys x 8 columns into 8 columns x 4 keys
-    const int pos = vt_pos(v_quad * 4);
-#pragma unroll
-    for (int e0 = 0; e0 < 8; ++e0) {
-      const int e = (e0 + v_chunk) & 7;  // rotate to spread LDS banks
-      const int m = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = pack_hi(vreg[0][m], vreg[1][m]);
-        hi = pack_hi(vreg[2][m], vreg[3][m]);
-      } else {
-        lo = pack_lo(vreg[0][m], vreg[1][m]);
-        hi = pack_lo(vreg[2][m], vreg[3][m]);
-      }
-      *reinterpret_cast<u32x2*>(Vt + (v_chunk * 8 + e) * T::VPITCH + pos) = u32x2{lo, hi};
-    }
-  };
-
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
+  }
+  __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);  // in flight while this tile is computed
-
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);   // that stage was last read in iteration j-1
+    if (j + 2 < n_tiles) load_tile(j + 2);          // in flight during this tile's compute
     const int kbase = j * BC;
-    if (CAUSAL && kbase > wave_last_key) continue;  // no row of this wave sees this tile
+    const __bf16* ks = Ks + (j & 1) * T::KSTAGE;
+    const __bf16* vs = Vs + (j & 1) * T::VSTAGE;
 
-    // ---- S^T = K_j Q^T for this wave's 32 rows ----
-    f32x16 s[BC / 32];
+    if (!CAUSAL || kbase <= wave_last_key) {
+      // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
+      f32x16 s[T::NKB];
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
-      s[kb] = f32x16{};
+      for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
+      bf16x8 kf[2][T::NKB];
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+        kf[0][kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * T::KP + 8 * hh);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * T::KPITCH + 16 * t + 8 * hh);
-        s[kb] = mfma32x32x16(kf, qf[t], s[kb]);
-      }
-    }
-
-    // ---- mask: ragged tail and the bottom-right causal edge ----
-    const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1;
+        if (t + 1 < D / 16) {
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+          for (int kb = 0; kb < T::NKB; ++kb)
+            kf[(t + 1) & 1][kb] =
+                *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * T::KP + 16 * (t + 1) + 8 * hh);
+        }
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+      }
+
+      // ---- mask: ragged tail and the bottom-right causal edge ----
+      const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
+      if (need_mask) {
+        const int thr = row_lim - kbase - 4 * hh;  // key offset in this lane's numbering
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) > thr) s[kb][r] = kNegInf;
+      }
+
+      // ---- online softmax (base 2, lazily rescaled) ----
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 32)) * scale_log2;
+      if (wave_any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
+        const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run - m_new);
+        l_run *= alpha;
+        lb_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) o[cb] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;  // a row with no key yet: all p = 0
+#pragma unroll
+      for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > lim) s[kb][r] = kNegInf;
+          s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+          l_run += s[kb][r];
         }
-    }
-
-    // ---- online softmax update (base 2) ----
-    float mx = kNegInf;
+      // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
+      bf16x8 pf[BC / 16];
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f_hw(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-        s[kb][r] = p;
-        psum += p;
+      for (int u = 0; u < BC / 16; ++u) {
+        const f32x16& sk = s[u >> 1];
+        const int r0 = (u & 1) * 8;
+        pf[u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
+                                sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
+        lb_run = sum_bf16x8(pf[u], lb_run);
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
 
-    // ---- O^T += V_j^T P^T ----
+      // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
+      // Fragment of column block cb, key step u (16 keys): lane (16-group g16, index i16)
+      // points at key 16u + 8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.
+      const __bf16* vbase = vs + (4 * hh + (i16 >> 2)) * T::VP + 16 * (g16 & 1) + 4 * (i16 & 3);
+      auto vfrag = [&](int u, int cb) {
+        const __bf16* p = vbase + (16 * u) * T::VP + 32 * cb;
+        return join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * T::VP));
+      };
+      bf16x8 vf[2][T::NCB];
 #pragma unroll
-    for (int u = 0; u < BC / 16; ++u) {
-      const f32x16& sk = s[u >> 1];
-      const int r0 = (u & 1) * 8;
-      const bf16x8 pf = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
-                                        sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
+      for (int cb = 0; cb < T::NCB; ++cb) vf[0][cb] = vfrag(0, cb);
 #pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (cb * 32 + l32) * T::VPITCH + 16 * u + 8 * hh);
-        o[cb] = mfma32x32x16(vf, pf, o[cb]);
+      for (int u = 0; u < BC / 16; ++u) {
+        if (u + 1 < BC / 16) {
+#pragma unroll
+          for (int cb = 0; cb < T::NCB; ++cb) vf[(u + 1) & 1][cb] = vfrag(u + 1, cb);
+        }
+#pragma unroll
+        for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
       }
     }
+    __syncthreads();  // tile j+1 visible; stage j&1 free for tile j+2
   }
 
   // ---- epilogue: one division, O and LSE written once ----
   const float l_tot = l_run + shfl_xor_f(l_run, 32);  // the two wave halves hold one row's keys
+  const float lb_tot = lb_run + shfl_xor_f(lb_run, 32);
   if (qrow >= N_q) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
   OutT* Orow = O + ((size_t)bh * N_q + qrow) * D;
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
+  for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int c = cb * 32 + 8 * g + 4 * hh;
