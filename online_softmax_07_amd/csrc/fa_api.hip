@@ -9,7 +9,7 @@
 namespace {
 
 constexpr int kNumCU = 256;        // MI355X compute units
-constexpr int kDecodeWGPerCU = 2;  // decode workgroups resident per CU (LDS/VGPR bound)
+constexpr int kDecodeWGPerCU = 1;  // one split workgroup per CU: more splits only grow the merge
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

@@ -13,13 +13,18 @@
 //     N_k - T + t and sees keys j <= N_k - T + t;
 //   * "The log-sum-exp merge": each split writes its normalized partial output and lse.
 //
-// Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a second row chunk goes
-// to blockIdx.z).  Each wave streams its own 64-key chunks of the split (chunks w, w+4,
-// ...), loads K straight into MFMA A fragments (16-byte loads), computes S^T = K Q^T
-// with the 16x16x32 bf16 MFMA (each lane then holds one row and 16 keys), runs the
-// online-softmax update, stages the chunk's V through a wave-private LDS area, transposed
-// while written, and accumulates O^T += V^T P^T.  At the end the four waves' carries
-// are merged in LDS by the same LSE rule.
+// Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk goes
+// to blockIdx.z).  Decode is a bytes problem, so the kernel is built around keeping loads
+// in flight: each wave streams its own 32-key chunks of the split (chunks w, w+4, ...),
+// and the loads of the next chunk are issued before the current one is computed (two
+// register sets).  K goes straight from memory into MFMA A fragments; V is written
+// row-major into a wave-private LDS area and read back as V^T with the transposing LDS
+// read.  S^T = K Q^T and O^T += V^T P^T run on the 16x16x32 bf16 MFMA (each lane holds
+// one row and 8 keys of a chunk).  Rows of keys past the split are loaded from a clamped
+// (valid) address and masked: their P is exactly 0, so no zero fill is needed.  With a
+// block table, every lane fetches the page of one key two chunks ahead and the row
+// addresses are exchanged with ds_bpermute, so the dependent table load never stalls the
+// stream.  At the end the four waves' carries are merged in LDS by the LSE rule.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -27,12 +32,17 @@ namespace fa {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecRows = 16;
+constexpr int kDecChunk = 32;  // keys per wave iteration
+static_assert(kDecChunk * 2 == kDecodeChunk, "split lengths are multiples of two chunks");
 
-// Position of key k (0 <= k < 64) inside a V^T row: key 32u + 16a + 4g + b goes to
-// 32u + 8g + 4a + b, making the 8 keys of one P^T k-group contiguous.
-__device__ __forceinline__ int dec_vt_pos(int k) {
-  return (k & 32) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
+template <int D>
+struct DecChunk {
+  static constexpr int KT = D / 32;                   // 16x16x32 k-steps over the head dimension
+  static constexpr int VL = kDecChunk * D / 8 / 64;   // 16-byte V pieces per lane
+  static constexpr int VROWS_PER_LOAD = 64 / (D / 8); // V rows covered by one load instruction
+  bf16x8 k[2][KT];
+  u32x4 v[VL];
+};
 
 template <int D, bool PAGED, typename OutT>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
@@ -41,12 +51,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     float* __restrict__ LSE_part, const int32_t* __restrict__ block_table, int page_size,
     int pages_per_seq, int H_q, int H_kv, int T, int N_k, int causal, int ns, int split_len,
     float scale_log2) {
-  constexpr int VPITCH = kDecodeChunk + 8;  // bf16 per V^T row (16-byte pad)
-  constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int VUNITS = (kDecodeChunk / 4) * CH / 64;  // 4-key x 8-col units per lane
-  constexpr int VT_BYTES = D * VPITCH * 2;
+  using C = DecChunk<D>;
+  constexpr int VP = D + 16;                          // V row pitch in LDS (32-byte pad)
+  constexpr int VT_ELEMS = kDecChunk * VP;            // per wave
   constexpr int MERGE_BYTES = (4 * kDecRows * 2 + 4 * kDecRows * D) * 4;
-  constexpr int SMEM = 4 * VT_BYTES > MERGE_BYTES ? 4 * VT_BYTES : MERGE_BYTES;
+  constexpr int SMEM = 4 * VT_ELEMS * 2 > MERGE_BYTES ? 4 * VT_ELEMS * 2 : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int split = blockIdx.x;
@@ -70,24 +79,50 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   const int hq = hk * g + hg;
   const int lim = causal ? N_k - T + tq : N_k - 1;  // last key this row sees (bottom-right)
 
-  bf16x8 qf[D / 32];
+  bf16x8 qf[C::KT];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    qf[t] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (((size_t)b * H_q + hq) * T + tq) * D + 32 * t + 8 * g4)
-                   : bf16x8{};
+  for (int t = 0; t < C::KT; ++t) {
+    qf[t] = *reinterpret_cast<const bf16x8*>(Q + (((size_t)b * H_q + hq) * T + tq) * D + 32 * t + 8 * g4);
+    if (!row_ok) qf[t] = bf16x8{};
   }
 
   const int k0 = split * split_len;
   const int k1 = min(k0 + split_len, N_k);
-  const int nchunks = k0 < k1 ? (k1 - k0 + kDecodeChunk - 1) / kDecodeChunk : 0;
+  const int nchunks = k0 < k1 ? (k1 - k0 + kDecChunk - 1) / kDecChunk : 0;
   const int min_lim = causal ? N_k - T : N_k - 1;  // smallest per-row limit
+  const int my_chunks = nchunks > wave ? (nchunks - wave + 3) / 4 : 0;  // chunks wave, wave+4, ...
 
-  auto key_row = [&](const __bf16* base, int key) -> const __bf16* {
+  // Row index (in units of D elements) of key `key` of this (b, hk).
+  auto row_of = [&](int key) -> int {
     if constexpr (PAGED) {
       const int page = block_table[(size_t)b * pages_per_seq + key / page_size];
-      return base + (((size_t)page * page_size + key % page_size) * H_kv + hk) * D;
+      return (page * page_size + key % page_size) * H_kv + hk;
     } else {
-      return base + ((size_t)bk * N_k + key) * D;
+      return bk * N_k + key;
+    }
+  };
+  // Each lane's share of a chunk's row indices: lane l holds key (cbase + l % 32), clamped
+  // into the split so every address is valid.
+  auto chunk_rows = [&](int i) -> int {
+    const int ci = wave + 4 * min(i, my_chunks - 1);
+    const int key = min(k0 + ci * kDecChunk + (lane & 31), k1 - 1);
+    return row_of(key);
+  };
+  auto load = [&](int rows, C& c) {
+    // K: lane (key l16 of block kb, k-group g4) -> MFMA A fragments
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = __builtin_amdgcn_ds_bpermute(4 * (kb * 16 + l16), rows);
+      const __bf16* kr = K + (size_t)r * D + 8 * g4;
+#pragma unroll
+      for (int t = 0; t < C::KT; ++t) c.k[kb][t] = *reinterpret_cast<const bf16x8*>(kr + 32 * t);
+    }
+    // V: load i covers VROWS_PER_LOAD whole rows, 16 bytes per lane
+#pragma unroll
+    for (int i = 0; i < C::VL; ++i) {
+      const int row = i * C::VROWS_PER_LOAD + lane / (D / 8);
+      const int r = __builtin_amdgcn_ds_bpermute(4 * row, rows);
+      c.v[i] = *reinterpret_cast<const u32x4*>(V + (size_t)r * D + (lane % (D / 8)) * 8);
     }
   };
 
@@ -95,61 +130,29 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   f32x4 o[D / 16];
 #pragma unroll
   for (int cb = 0; cb < D / 16; ++cb) o[cb] = f32x4{};
+  __bf16* Vt = reinterpret_cast<__bf16*>(smem) + wave * VT_ELEMS;
 
-  __bf16* Vt = reinterpret_cast<__bf16*>(smem) + wave * D * VPITCH;
-
-  for (int ci = wave; ci < nchunks; ci += 4) {
-    const int cbase = k0 + ci * kDecodeChunk;
-
-    // ---- loads: K as MFMA A fragments, V as 4-row x 8-column units ----
-    bf16x8 kf[4][D / 32];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = cbase + kb * 16 + l16;
-      if (key < k1) {
-        const __bf16* kr = key_row(K, key);
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) kf[kb][t] = *reinterpret_cast<const bf16x8*>(kr + 32 * t + 8 * g4);
-      } else {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) kf[kb][t] = bf16x8{};
-      }
-    }
-    u32x4 vreg[VUNITS][4];
-#pragma unroll
-    for (int i = 0; i < VUNITS; ++i) {
-      const int u = i * 64 + lane;
-      const int quad = u / CH;
-      const int chunk = u % CH;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = cbase + quad * 4 + r;
-        vreg[i][r] = key < k1 ? *reinterpret_cast<const u32x4*>(key_row(V, key) + chunk * 8) : u32x4{};
-      }
-    }
-
+  auto compute = [&](int i, C& c) {
+    const int cbase = k0 + (wave + 4 * i) * kDecChunk;
     // ---- S^T = K Q^T: lane holds row l16, keys 16 kb + 4 g4 + r ----
-    f32x4 s[4];
+    f32x4 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{};
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) s[kb] = mfma16x16x32(kf[kb][t], qf[t], s[kb]);
+      for (int t = 0; t < C::KT; ++t) s[kb] = mfma16x16x32(c.k[kb][t], qf[t], s[kb]);
     }
-    if (cbase + kDecodeChunk > k1 || cbase + kDecodeChunk - 1 > min_lim) {
+    if (cbase + kDecChunk > k1 || cbase + kDecChunk - 1 > min_lim) {
       const int last = min(k1 - 1, lim);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (cbase + kb * 16 + 4 * g4 + r > last) s[kb][r] = kNegInf;
     }
-
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+    // ---- online softmax (exact running max) ----
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float m_new = fmaxf(m_run, mx * scale_log2);
@@ -157,61 +160,62 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const float alpha = exp2f_hw(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
         psum += s[kb][r];
       }
     l_run = l_run * alpha + psum;
-    // P^T operands (bf16, RNE) for the two 32-key steps
-    bf16x8 pf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      pf[u] = to_bf16x8(f32x8{s[2 * u][0], s[2 * u][1], s[2 * u][2], s[2 * u][3],
-                              s[2 * u + 1][0], s[2 * u + 1][1], s[2 * u + 1][2], s[2 * u + 1][3]});
     m_run = m_new;
 #pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) o[cb] *= alpha;
+    // P^T operand: slots 0-3 = keys 4 g4 + r, slots 4-7 = keys 16 + 4 g4 + r
+    const bf16x8 pf = to_bf16x8(f32x8{s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]});
 
-    // ---- V chunk -> wave-private LDS, transposed to V^T ----
+    // ---- V chunk -> wave-private LDS, row-major ----
 #pragma unroll
-    for (int i = 0; i < VUNITS; ++i) {
-      const int u = i * 64 + lane;
-      const int quad = u / CH;
-      const int chunk = u % CH;
-      const int pos = dec_vt_pos(quad * 4);
-#pragma unroll
-      for (int e0 = 0; e0 < 8; ++e0) {
-        const int e = (e0 + chunk) & 7;
-        const int m = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = pack_hi(vreg[i][0][m], vreg[i][1][m]);
-          hi = pack_hi(vreg[i][2][m], vreg[i][3][m]);
-        } else {
-          lo = pack_lo(vreg[i][0][m], vreg[i][1][m]);
-          hi = pack_lo(vreg[i][2][m], vreg[i][3][m]);
-        }
-        *reinterpret_cast<u32x2*>(Vt + (chunk * 8 + e) * VPITCH + pos) = u32x2{lo, hi};
-      }
+    for (int i2 = 0; i2 < C::VL; ++i2) {
+      const int row = i2 * C::VROWS_PER_LOAD + lane / (D / 8);
+      *reinterpret_cast<u32x4*>(Vt + row * VP + (lane % (D / 8)) * 8) = c.v[i2];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- O^T += V^T P^T (two k-steps of 32 keys) ----
+    // ---- O^T += V^T P^T: A fragment (cb) via two transposing reads.  Lane (16-group g4,
+    // index l16) points at key 16 r + 4 g4 + l16/4, columns 16 cb + 4 (l16 % 4) .. +3.
+    const __bf16* vb = Vt + (4 * g4 + (l16 >> 2)) * VP + 4 * (l16 & 3);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (cb * 16 + l16) * VPITCH + 32 * u + 8 * g4);
-        o[cb] = mfma16x16x32(vf, pf[u], o[cb]);
-      }
+    for (int cb = 0; cb < D / 16; ++cb) {
+      const bf16x8 vf = join_bf16x8(lds_read_tr16(vb + 16 * cb), lds_read_tr16(vb + 16 * VP + 16 * cb));
+      o[cb] = mfma16x16x32(vf, pf, o[cb]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- the stream: loads of chunk i+1 in flight while chunk i is computed; table rows
+  // (paged) fetched one chunk earlier still ----
+  if (my_chunks > 0) {
+    C ca, cb_;
+    int rows_next = chunk_rows(0);
+    int rows_after = chunk_rows(1);
+    load(rows_next, ca);
+    rows_next = rows_after;
+    rows_after = chunk_rows(2);
+    int i = 0;
+    for (; i + 1 < my_chunks; i += 2) {
+      load(rows_next, cb_);
+      rows_next = rows_after;
+      rows_after = chunk_rows(i + 3);
+      compute(i, ca);
+      if (i + 2 < my_chunks) load(rows_next, ca);
+      rows_next = rows_after;
+      rows_after = chunk_rows(i + 4);
+      compute(i + 1, cb_);
+    }
+    if (i < my_chunks) compute(i, ca);
   }
 
   // ---- merge the four waves (same LSE rule, in base 2) ----

@@ -36,7 +36,8 @@ class FAError(RuntimeError):
 
 
 def library_path() -> str:
-    return _build.LIB
+    """The in-tree build, or the file named by FA_MI355X_LIB (an alternative build)."""
+    return os.environ.get("FA_MI355X_LIB") or _build.LIB
 
 
 def lib() -> ctypes.CDLL:
@@ -44,12 +45,14 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build(verbose=False)
-    elif _build.is_stale():
-        sys.stderr.write(f"warning: {_build.LIB} is older than its sources; "
-                         "run `python -m online_softmax_07_amd.build`\n")
-    L = ctypes.CDLL(_build.LIB)
+    path = library_path()
+    if path == _build.LIB:
+        if not os.path.exists(path):
+            _build.build(verbose=False)
+        elif _build.is_stale():
+            sys.stderr.write(f"warning: {path} is older than its sources; "
+                             "run `python -m online_softmax_07_amd.build`\n")
+    L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.fa_fwd.restype = i
