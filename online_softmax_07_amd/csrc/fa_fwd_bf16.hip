@@ -30,6 +30,8 @@
 //     wave-uniform).  O is divided by the sum of the same bf16-rounded P the PV product
 //     uses (v_dot2 against (1, 1)), so the rounding of a dominant weight (which need not
 //     be 1 under a lagging max) cancels in O = sum p V / sum p; the LSE uses the fp32 sum.
+//   * The wave raises its issue priority for its MFMA sections (s_setprio), so the two
+//     waves sharing a SIMD tend to alternate: one on the matrix core, one on the VALU.
 //   * Workgroup order: heaviest causal query blocks first, and consecutive blocks of a
 //     head kept on one XCD so the K/V re-reads of the FlashAttention-2 order hit its L2.
 //   * Softmax in base 2: p = 2^(s * scale * log2 e - m), with m kept in the same units.
@@ -169,6 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     if (!CAUSAL || kbase <= wave_last_key) {
       // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
+      __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
       f32x16 s[T::NKB];
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // ---- mask: ragged tail and the bottom-right causal edge ----
       const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
       if (need_mask) {
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       bf16x8 vf[2][T::NCB];
 #pragma unroll
       for (int cb = 0; cb < T::NCB; ++cb) vf[0][cb] = vfrag(0, cb);
+      __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
 #pragma unroll
       for (int u = 0; u < BC / 16; ++u) {
         if (u + 1 < BC / 16) {
@@ -255,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();  // tile j+1 visible; stage j&1 free for tile j+2
   }
