@@ -106,6 +106,18 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L of the wave writes
+// lds_wave_base + 16 L bytes (lds_wave_base must be wave-uniform); lanes whose offset is
+// out of the descriptor's range write zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                                  __bf16* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voffset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave (LDS DMAs included) has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Bytes from element `start` to the end of a range of `n` rows of `row_bytes`, clamped to
 // the 32-bit descriptor range.
 __device__ __forceinline__ uint32_t range_bytes(long long rows_left, int row_bytes) {

@@ -18,10 +18,10 @@
 //   * O^T = V^T P^T on the same MFMA: P^T comes straight from the score registers
 //     (converted to bf16); V^T fragments are read from the row-major V tile in LDS with
 //     the transposing LDS read (ds_read_b64_tr_b16), so V is staged exactly like K.
-//   * K/V tiles: coalesced 16-byte raw buffer loads (zero past the end of the sequence)
-//     held in registers one tile ahead, then written to a double-buffered LDS ring; one
-//     barrier per tile.  Row pitches are padded
-//     so the MFMA operand reads (plain for K, transposing for V) are bank-conflict free.
+//   * K/V tiles: 16-byte buffer loads that write LDS directly (no register staging), one
+//     tile ahead into a double-buffered LDS ring; zero past the end of the sequence; one
+//     barrier per tile.  Rows are stored unpadded with a 16-byte-chunk XOR swizzle that
+//     keeps the MFMA operand reads (plain for K, transposing for V) bank-conflict free.
 //   * Independent accumulators are interleaved and operand fragments are read one step
 //     ahead of the MFMA that consumes them.
 //   * The running max is only moved (and l, O rescaled) when a row's tile max exceeds it
@@ -46,15 +46,19 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag beh
 
 template <int D, int BC>
 struct FwdTile {
-  static constexpr int KP = D + 8;          // K row pitch (bf16): 16-byte pad -> plain b128 reads conflict free
-  static constexpr int VP = D + 16;         // V row pitch: 32-byte pad -> transposing reads conflict free
   static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
-  static constexpr int LOADS = BC * CHUNKS / kThreads;  // chunks per thread per tile, for K and for V
+  static constexpr int STAGE = BC * D;      // elements of one K or V stage (no padding)
+  static constexpr int ROWS_PER_DMA = 1024 / (2 * D);   // rows one wave-wide 16-byte DMA fills
+  static constexpr int DMA = BC * D * 2 / 1024 / (kThreads / 64);  // DMAs per wave per tile (K, V each)
   static constexpr int NKB = BC / 32;       // 32-key blocks per tile
   static constexpr int NCB = D / 32;        // 32-column blocks of O^T
-  static constexpr int KSTAGE = BC * KP;
-  static constexpr int VSTAGE = BC * VP;
-  static_assert(BC * CHUNKS % kThreads == 0, "tile must split evenly over the threads");
+  static_assert(DMA * 1024 * (kThreads / 64) == BC * D * 2, "tile must split evenly over the waves");
+  // Logical 16-byte chunk c of row r sits at position c ^ swz(r) of the row.  Rows are not
+  // padded (a DMA fills 1 KiB contiguously); the swizzle spreads both the plain K reads
+  // (16 rows, one chunk) and the transposing V reads (4 rows x 4 chunks) over all banks.
+  static __device__ __forceinline__ int swz(int r) {
+    return D == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
 };
 
 template <int D, int BC, bool CAUSAL, typename OutT>
@@ -63,8 +67,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
     float scale_log2, int n_qblocks, int total_wg) {
   using T = FwdTile<D, BC>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * T::KSTAGE];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2 * T::VSTAGE];
+  // Two K and two V stages as separate arrays: with the stage known at compile time the
+  // compiler can tell that a tile's LDS reads do not touch the stage being refilled, and
+  // does not wait for the refill before reading.
+  __shared__ __attribute__((aligned(16))) __bf16 Ks0[T::STAGE], Ks1[T::STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs0[T::STAGE], Vs1[T::STAGE];
 
   // ---- which (batch, head, query block) this workgroup owns ----
   const int wg = blockIdx.x;
@@ -119,55 +126,58 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
   for (int cb = 0; cb < T::NCB; ++cb) o[cb] = f32x16{};
 
-  // ---- K/V staging: global -> registers -> LDS stage ----
-  // Raw buffer loads with a descriptor that starts at the tile and ends at N_k: rows past
-  // the end of the sequence read as zeros (K: scores that get masked; V: 0 * V = 0).
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  uint32_t goff[T::LOADS];   // byte offset of this thread's chunks inside a tile
-  int loff_k[T::LOADS], loff_v[T::LOADS];  // and their element offsets in an LDS stage
+  // ---- K/V staging: global -> LDS directly (16-byte buffer loads with an LDS target) ----
+  // Wave w's DMA i fills rows ROWS_PER_DMA * (DMA * w + i) + lane / CHUNKS; the lane fetches
+  // the logical chunk that belongs at its position.  The descriptor starts at the tile and
+  // ends at N_k: rows past the end of the sequence arrive as zeros (K: scores that get
+  // masked; V: 0 * V = 0).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t dma_off[T::DMA];
 #pragma unroll
-  for (int i = 0; i < T::LOADS; ++i) {
-    const int c = i * kThreads + tid;
-    const int row = c / T::CHUNKS;
-    const int col = c % T::CHUNKS;
-    goff[i] = (uint32_t)(row * D + col * 8) * 2u;
-    loff_k[i] = row * T::KP + col * 8;
-    loff_v[i] = row * T::VP + col * 8;
+  for (int i = 0; i < T::DMA; ++i) {
+    const int r = T::ROWS_PER_DMA * (T::DMA * wave + i) + lane / T::CHUNKS;
+    const int pos = lane % T::CHUNKS;
+    dma_off[i] = (uint32_t)(r * D + 8 * (pos ^ T::swz(r))) * 2u;
   }
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j, __bf16* ks, __bf16* vs) {
     const int kbase = j * BC;
     const uint32_t bytes = range_bytes((long long)N_k - kbase, D * 2);
     const auto kr = make_rsrc(Kp + (size_t)kbase * D, bytes);
     const auto vr = make_rsrc(Vp + (size_t)kbase * D, bytes);
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      kreg[i] = buffer_load16(kr, goff[i]);
-      vreg[i] = buffer_load16(vr, goff[i]);
+    for (int i = 0; i < T::DMA; ++i) {
+      const int dst = (T::DMA * wave_u + i) * 512;
+      buffer_load16_lds(kr, dma_off[i], ks + dst);
+      buffer_load16_lds(vr, dma_off[i], vs + dst);
     }
   };
-  auto store_tile = [&](int stage) {
-    __bf16* ks = Ks + stage * T::KSTAGE;
-    __bf16* vs = Vs + stage * T::VSTAGE;
+  // LDS read offsets (elements) of this lane's MFMA operands in a stage.  K fragment of
+  // 32-key block kb, k-step t: row kb*32 + l32, logical chunk 2t + hh.  V^T fragment of
+  // column block cb, key step u, half r: lane (16-group g16, index i16) points at key
+  // 16u + 8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.  The swizzle of a
+  // row depends only on its index mod 16, so kb and u enter as plain immediates.
+  int koff[D / 16];
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      *reinterpret_cast<u32x4*>(ks + loff_k[i]) = kreg[i];
-      *reinterpret_cast<u32x4*>(vs + loff_v[i]) = vreg[i];
+  for (int t = 0; t < D / 16; ++t) koff[t] = l32 * D + 8 * ((2 * t + hh) ^ T::swz(l32));
+  int voff[2][T::NCB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int cb = 0; cb < T::NCB; ++cb) {
+      const int row = 8 * r + 4 * hh + (i16 >> 2);
+      const int c = 4 * cb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      voff[r][cb] = row * D + 8 * (c ^ T::swz(row)) + 4 * (i16 & 1);
     }
-  };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
-  }
+  if (n_tiles > 0) load_tile(0, Ks0, Vs0);
+  wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);   // that stage was last read in iteration j-1
-    if (j + 2 < n_tiles) load_tile(j + 2);          // in flight during this tile's compute
+  // Tile j reads stage (ks, vs) while tile j+1 streams into (ks_next, vs_next), which
+  // tile j-1 read before the last barrier.
+  auto tile_step = [&](int j, const __bf16* ks, const __bf16* vs, __bf16* ks_next, __bf16* vs_next) {
+    if (j + 1 < n_tiles) load_tile(j + 1, ks_next, vs_next);
     const int kbase = j * BC;
-    const __bf16* ks = Ks + (j & 1) * T::KSTAGE;
-    const __bf16* vs = Vs + (j & 1) * T::VSTAGE;
 
     if (!CAUSAL || kbase <= wave_last_key) {
       // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
@@ -178,14 +188,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       bf16x8 kf[2][T::NKB];
 #pragma unroll
       for (int kb = 0; kb < T::NKB; ++kb)
-        kf[0][kb] = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * T::KP + 8 * hh);
+        kf[0][kb] = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         if (t + 1 < D / 16) {
 #pragma unroll
           for (int kb = 0; kb < T::NKB; ++kb)
             kf[(t + 1) & 1][kb] =
-                *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + l32) * T::KP + 16 * (t + 1) + 8 * hh);
+                *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[t + 1]);
         }
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
@@ -240,12 +250,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
 
       // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
-      // Fragment of column block cb, key step u (16 keys): lane (16-group g16, index i16)
-      // points at key 16u + 8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.
-      const __bf16* vbase = vs + (4 * hh + (i16 >> 2)) * T::VP + 16 * (g16 & 1) + 4 * (i16 & 3);
       auto vfrag = [&](int u, int cb) {
-        const __bf16* p = vbase + (16 * u) * T::VP + 32 * cb;
-        return join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * T::VP));
+        const __bf16* p = vs + 16 * u * D;
+        return join_bf16x8(lds_read_tr16(p + voff[0][cb]), lds_read_tr16(p + voff[1][cb]));
       };
       bf16x8 vf[2][T::NCB];
 #pragma unroll
@@ -262,7 +269,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    __syncthreads();  // tile j+1 visible; stage j&1 free for tile j+2
+    wait_vmem();      // this wave's DMAs of tile j+1 have landed
+    __syncthreads();  // everyone's have; stage (ks, vs) is free for tile j+2
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile_step(j, Ks0, Vs0, Ks1, Vs1);
+    if (j + 1 < n_tiles) tile_step(j + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
   // ---- epilogue: one division, O and LSE written once ----
