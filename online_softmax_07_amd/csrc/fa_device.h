@@ -43,6 +43,12 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
 
+// max(x, x of lane l ^ 32): the two halves of the wave swapped by one v_permlane32_swap.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Pack halves: result = (hi16 of b or lo16 of b) << 16 | (same half of a).
 // Used to transpose 4x(8 bf16) row chunks into 8x(4 bf16) column chunks.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {

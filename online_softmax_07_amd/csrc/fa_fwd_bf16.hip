@@ -32,8 +32,9 @@
 //     be 1 under a lagging max) cancels in O = sum p V / sum p; the LSE uses the fp32 sum.
 //   * The wave raises its issue priority for its MFMA sections (s_setprio), so the two
 //     waves sharing a SIMD tend to alternate: one on the matrix core, one on the VALU.
-//   * Workgroup order: heaviest causal query blocks first, and consecutive blocks of a
-//     head kept on one XCD so the K/V re-reads of the FlashAttention-2 order hit its L2.
+//   * Workgroup order: each XCD owns a range of heads, so the K/V re-reads of the
+//     FlashAttention-2 order hit its L2; causal blocks are dispatched heaviest first
+//     across the XCD's heads.
 //   * Softmax in base 2: p = 2^(s * scale * log2 e - m), with m kept in the same units.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -74,11 +75,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 Vs0[T::STAGE], Vs1[T::STAGE];
 
   // ---- which (batch, head, query block) this workgroup owns ----
+  // Workgroups are dispatched round-robin over the 8 XCDs (workgroup wg runs on XCD wg % 8).
+  // Each XCD gets a contiguous range of heads, so the K/V re-reads of a head stay in one
+  // L2.  Within an XCD, causal blocks go heaviest first across all of its heads (longest
+  // first: block costs range from 1 to n_qblocks units, and a head-by-head order would
+  // start the last head's heavy blocks late and leave a long tail); full attention, whose
+  // blocks all cost the same, goes head by head.
   const int wg = blockIdx.x;
-  int logical = wg;
-  if ((total_wg & 7) == 0) logical = (wg & 7) * (total_wg >> 3) + (wg >> 3);  // XCD-contiguous
-  const int bh = logical / n_qblocks;
-  const int qb = n_qblocks - 1 - (logical % n_qblocks);  // heavy (late) blocks first
+  const int n_bh = total_wg / n_qblocks;
+  int bh, qb;
+  if ((n_bh & 7) == 0) {
+    const int hpx = n_bh >> 3;            // heads per XCD
+    const int x = wg & 7, idx = wg >> 3;  // XCD, and position in its dispatch order
+    if (CAUSAL) {
+      bh = x * hpx + idx % hpx;
+      qb = n_qblocks - 1 - idx / hpx;
+    } else {
+      bh = x * hpx + idx / n_qblocks;
+      qb = idx % n_qblocks;
+    }
+  } else {
+    int logical = wg;
+    if ((total_wg & 7) == 0) logical = (wg & 7) * (total_wg >> 3) + (wg >> 3);  // XCD-contiguous
+    bh = logical / n_qblocks;
+    qb = n_qblocks - 1 - (logical % n_qblocks);  // heavy (late) blocks first
+  }
   const int b = bh / H_q;
   const int h = bh - b * H_q;
   const int hk = h / (H_q / H_kv);
@@ -219,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 32)) * scale_log2;
+      mx = max_halves(mx) * scale_log2;
       if (wave_any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
         // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
