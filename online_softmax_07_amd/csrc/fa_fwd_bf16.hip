@@ -19,8 +19,8 @@
 //     (converted to bf16); V^T fragments are read from the row-major V tile in LDS with
 //     the transposing LDS read (ds_read_b64_tr_b16), so V is staged exactly like K.
 //   * K/V tiles: 16-byte buffer loads that write LDS directly (no register staging), one
-//     tile ahead into a double-buffered LDS ring; zero past the end of the sequence; one
-//     barrier per tile.  Rows are stored unpadded with a 16-byte-chunk XOR swizzle that
+//     tile ahead into a double-buffered LDS ring, issued a few at a time between the
+//     score MFMAs; zero past the end of the sequence; one barrier per tile.  Rows are stored unpadded with a 16-byte-chunk XOR swizzle that
 //     keeps the MFMA operand reads (plain for K, transposing for V) bank-conflict free.
 //   * Independent accumulators are interleaved and operand fragments are read one step
 //     ahead of the MFMA that consumes them.
@@ -160,17 +160,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int pos = lane % T::CHUNKS;
     dma_off[i] = (uint32_t)(r * D + 8 * (pos ^ T::swz(r))) * 2u;
   }
-  auto load_tile = [&](int j, __bf16* ks, __bf16* vs) {
+  // DMA i (0 .. 2*DMA-1) of tile j: the K rows first, then the V rows.  Past the end of the
+  // sequence the descriptor is empty and the stage receives zeros.
+  auto tile_rsrc = [&](const __bf16* base, int j) {
     const int kbase = j * BC;
-    const uint32_t bytes = range_bytes((long long)N_k - kbase, D * 2);
-    const auto kr = make_rsrc(Kp + (size_t)kbase * D, bytes);
-    const auto vr = make_rsrc(Vp + (size_t)kbase * D, bytes);
-#pragma unroll
-    for (int i = 0; i < T::DMA; ++i) {
-      const int dst = (T::DMA * wave_u + i) * 512;
-      buffer_load16_lds(kr, dma_off[i], ks + dst);
-      buffer_load16_lds(vr, dma_off[i], vs + dst);
-    }
+    return make_rsrc(base + (size_t)kbase * D, range_bytes((long long)N_k - kbase, D * 2));
+  };
+  auto dma = [&](int i, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, __bf16* ks, __bf16* vs) {
+    const int ii = i % T::DMA;
+    const int dst = (T::DMA * wave_u + ii) * 512;
+    if (i < T::DMA) buffer_load16_lds(kr, dma_off[ii], ks + dst);
+    else buffer_load16_lds(vr, dma_off[ii], vs + dst);
   };
   // LDS read offsets (elements) of this lane's MFMA operands in a stage.  K fragment of
   // 32-key block kb, k-step t: row kb*32 + l32, logical chunk 2t + hh.  V^T fragment of
@@ -190,14 +190,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       voff[r][cb] = row * D + 8 * (c ^ T::swz(row)) + 4 * (i16 & 1);
     }
 
-  if (n_tiles > 0) load_tile(0, Ks0, Vs0);
+  if (n_tiles > 0) {
+    const auto kr = tile_rsrc(Kp, 0), vr = tile_rsrc(Vp, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * T::DMA; ++i) dma(i, kr, vr, Ks0, Vs0);
+  }
   wait_vmem();
   __syncthreads();
 
   // Tile j reads stage (ks, vs) while tile j+1 streams into (ks_next, vs_next), which
   // tile j-1 read before the last barrier.
   auto tile_step = [&](int j, const __bf16* ks, const __bf16* vs, __bf16* ks_next, __bf16* vs_next) {
-    if (j + 1 < n_tiles) load_tile(j + 1, ks_next, vs_next);
+    // Tile j+1 streams into (ks_next, vs_next), which tile j-1 read before the last
+    // barrier.  Its DMAs are issued a few at a time between the score MFMAs: a wave that
+    // issued them all at once would sit at the first one whose queue slot is not free.
+    // (After the last tile the descriptors are empty: the stage gets zeros nobody reads.)
+    const auto kr_next = tile_rsrc(Kp, j + 1), vr_next = tile_rsrc(Vp, j + 1);
+    constexpr int NDMA = 2 * T::DMA;
+    constexpr int DMA_PER_STEP = (NDMA + D / 16 - 1) / (D / 16);
     const int kbase = j * BC;
 
     if (!CAUSAL || kbase <= wave_last_key) {
@@ -220,6 +230,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+#pragma unroll
+        for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
+          dma(i, kr_next, vr_next, ks_next, vs_next);
       }
 
       __builtin_amdgcn_s_setprio(0);
@@ -289,6 +302,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
       }
       __builtin_amdgcn_s_setprio(0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) dma(i, kr_next, vr_next, ks_next, vs_next);
     }
     wait_vmem();      // this wave's DMAs of tile j+1 have landed
     __syncthreads();  // everyone's have; stage (ks, vs) is free for tile j+2
