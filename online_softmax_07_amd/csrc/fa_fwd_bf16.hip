@@ -32,9 +32,10 @@
 //     be 1 under a lagging max) cancels in O = sum p V / sum p; the LSE uses the fp32 sum.
 //   * The wave raises its issue priority for its MFMA sections (s_setprio), so the two
 //     waves sharing a SIMD tend to alternate: one on the matrix core, one on the VALU.
-//   * Workgroup order: each XCD owns a range of heads, so the K/V re-reads of the
-//     FlashAttention-2 order hit its L2; causal blocks are dispatched heaviest first
-//     across the XCD's heads.
+//   * Workgroup order: each XCD owns a range of heads and works through them head by
+//     head, so the K/V re-reads of the FlashAttention-2 order hit its L2.  A causal
+//     workgroup takes two query blocks, the i-th heaviest and the i-th lightest of a head,
+//     so that all workgroups cost the same.
 //   * Softmax in base 2: p = 2^(s * scale * log2 e - m), with m kept in the same units.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -66,7 +67,7 @@ template <int D, int BC, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
-    float scale_log2, int n_qblocks, int total_wg) {
+    float scale_log2, int n_qblocks, int n_units, int total_wg) {
   using T = FwdTile<D, BC>;
   // Two K and two V stages as separate arrays: with the stage known at compile time the
   // compiler can tell that a tile's LDS reads do not touch the stage being refilled, and
@@ -76,29 +77,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
   // ---- which (batch, head, query block) this workgroup owns ----
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup wg runs on XCD wg % 8).
-  // Each XCD gets a contiguous range of heads, so the K/V re-reads of a head stay in one
-  // L2.  Within an XCD, causal blocks go heaviest first across all of its heads (longest
-  // first: block costs range from 1 to n_qblocks units, and a head-by-head order would
-  // start the last head's heavy blocks late and leave a long tail); full attention, whose
-  // blocks all cost the same, goes head by head.
+  // Each XCD gets a contiguous range of heads and works through them head by head, so the
+  // K/V re-reads of the FlashAttention-2 order stay in its L2.  Causal blocks differ in
+  // cost (query block i visits about i+1 tiles), so a causal workgroup takes a pair of
+  // blocks, the i-th heaviest and the i-th lightest of a head: every pair costs the same,
+  // and no expensive block is left to start late.
   const int wg = blockIdx.x;
-  const int n_bh = total_wg / n_qblocks;
-  int bh, qb;
+  const int n_bh = total_wg / n_units;
+  int bh, unit;
   if ((n_bh & 7) == 0) {
     const int hpx = n_bh >> 3;            // heads per XCD
     const int x = wg & 7, idx = wg >> 3;  // XCD, and position in its dispatch order
-    if (CAUSAL) {
-      bh = x * hpx + idx % hpx;
-      qb = n_qblocks - 1 - idx / hpx;
-    } else {
-      bh = x * hpx + idx / n_qblocks;
-      qb = idx % n_qblocks;
-    }
+    bh = x * hpx + idx / n_units;
+    unit = idx % n_units;
   } else {
     int logical = wg;
     if ((total_wg & 7) == 0) logical = (wg & 7) * (total_wg >> 3) + (wg >> 3);  // XCD-contiguous
-    bh = logical / n_qblocks;
-    qb = n_qblocks - 1 - (logical % n_qblocks);  // heavy (late) blocks first
+    bh = logical / n_units;
+    unit = logical % n_units;
   }
   const int b = bh / H_q;
   const int h = bh - b * H_q;
@@ -114,239 +110,245 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int hh = lane >> 5;      // k-group of the MFMA operands
   const int g16 = lane >> 4;     // 16-lane group (transposing reads)
   const int i16 = lane & 15;
-  const int q0 = qb * kBR;
-  const int wave_row0 = q0 + wave * 32;
-  const int qrow = wave_row0 + l32;
-  const int shift = N_k - N_q;   // bottom-right alignment: row i sees keys j <= i + shift
+  const int n_pass = (CAUSAL && 2 * unit + 1 < n_qblocks) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int qb = !CAUSAL ? unit : (pass == 0 ? n_qblocks - 1 - unit : unit);
+    const int q0 = qb * kBR;
+    const int wave_row0 = q0 + wave * 32;
+    const int qrow = wave_row0 + l32;
+    const int shift = N_k - N_q;   // bottom-right alignment: row i sees keys j <= i + shift
 
-  // ---- Q block: read once, kept as MFMA B fragments ----
-  bf16x8 qf[D / 16];
-  {
-    const int qr = qrow < N_q ? qrow : N_q - 1;  // clamped row; zeroed below
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      qf[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qr * D + 16 * t + 8 * hh);
-      if (qrow >= N_q) qf[t] = bf16x8{};
-    }
-  }
-
-  // ---- which K/V tiles this block visits ----
-  int n_tiles = (N_k + BC - 1) / BC;
-  if (CAUSAL) {
-    const int max_key = min(q0 + kBR - 1, N_q - 1) + shift;
-    n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
-  }
-  const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;  // causal reach of this wave
-  const int row_lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1; // last key this row sees
-
-  // ---- carries ----
-  float m_run = kNegInf;  // reference max (log2 units of the scaled scores)
-  float l_run = 0.f;      // this lane's partial sum of p over its keys (fp32 p: for the LSE)
-  float lb_run = 0.f;     // the same sum over the bf16-rounded p the PV product uses (for O)
-  f32x16 o[T::NCB];
-#pragma unroll
-  for (int cb = 0; cb < T::NCB; ++cb) o[cb] = f32x16{};
-
-  // ---- K/V staging: global -> LDS directly (16-byte buffer loads with an LDS target) ----
-  // Wave w's DMA i fills rows ROWS_PER_DMA * (DMA * w + i) + lane / CHUNKS; the lane fetches
-  // the logical chunk that belongs at its position.  The descriptor starts at the tile and
-  // ends at N_k: rows past the end of the sequence arrive as zeros (K: scores that get
-  // masked; V: 0 * V = 0).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t dma_off[T::DMA];
-#pragma unroll
-  for (int i = 0; i < T::DMA; ++i) {
-    const int r = T::ROWS_PER_DMA * (T::DMA * wave + i) + lane / T::CHUNKS;
-    const int pos = lane % T::CHUNKS;
-    dma_off[i] = (uint32_t)(r * D + 8 * (pos ^ T::swz(r))) * 2u;
-  }
-  // DMA i (0 .. 2*DMA-1) of tile j: the K rows first, then the V rows.  Past the end of the
-  // sequence the descriptor is empty and the stage receives zeros.
-  auto tile_rsrc = [&](const __bf16* base, int j) {
-    const int kbase = j * BC;
-    return make_rsrc(base + (size_t)kbase * D, range_bytes((long long)N_k - kbase, D * 2));
-  };
-  auto dma = [&](int i, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, __bf16* ks, __bf16* vs) {
-    const int ii = i % T::DMA;
-    const int dst = (T::DMA * wave_u + ii) * 512;
-    if (i < T::DMA) buffer_load16_lds(kr, dma_off[ii], ks + dst);
-    else buffer_load16_lds(vr, dma_off[ii], vs + dst);
-  };
-  // LDS read offsets (elements) of this lane's MFMA operands in a stage.  K fragment of
-  // 32-key block kb, k-step t: row kb*32 + l32, logical chunk 2t + hh.  V^T fragment of
-  // column block cb, key step u, half r: lane (16-group g16, index i16) points at key
-  // 16u + 8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.  The swizzle of a
-  // row depends only on its index mod 16, so kb and u enter as plain immediates.
-  int koff[D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) koff[t] = l32 * D + 8 * ((2 * t + hh) ^ T::swz(l32));
-  int voff[2][T::NCB];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int cb = 0; cb < T::NCB; ++cb) {
-      const int row = 8 * r + 4 * hh + (i16 >> 2);
-      const int c = 4 * cb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      voff[r][cb] = row * D + 8 * (c ^ T::swz(row)) + 4 * (i16 & 1);
-    }
-
-  if (n_tiles > 0) {
-    const auto kr = tile_rsrc(Kp, 0), vr = tile_rsrc(Vp, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * T::DMA; ++i) dma(i, kr, vr, Ks0, Vs0);
-  }
-  wait_vmem();
-  __syncthreads();
-
-  // Tile j reads stage (ks, vs) while tile j+1 streams into (ks_next, vs_next), which
-  // tile j-1 read before the last barrier.
-  auto tile_step = [&](int j, const __bf16* ks, const __bf16* vs, __bf16* ks_next, __bf16* vs_next) {
-    // Tile j+1 streams into (ks_next, vs_next), which tile j-1 read before the last
-    // barrier.  Its DMAs are issued a few at a time between the score MFMAs: a wave that
-    // issued them all at once would sit at the first one whose queue slot is not free.
-    // (After the last tile the descriptors are empty: the stage gets zeros nobody reads.)
-    const auto kr_next = tile_rsrc(Kp, j + 1), vr_next = tile_rsrc(Vp, j + 1);
-    constexpr int NDMA = 2 * T::DMA;
-    constexpr int DMA_PER_STEP = (NDMA + D / 16 - 1) / (D / 16);
-    const int kbase = j * BC;
-
-    if (!CAUSAL || kbase <= wave_last_key) {
-      // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
-      __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
-      f32x16 s[T::NKB];
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
-      bf16x8 kf[2][T::NKB];
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-        kf[0][kb] = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]);
+    // ---- Q block: read once, kept as MFMA B fragments ----
+    bf16x8 qf[D / 16];
+    {
+      const int qr = qrow < N_q ? qrow : N_q - 1;  // clamped row; zeroed below
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        if (t + 1 < D / 16) {
+        qf[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qr * D + 16 * t + 8 * hh);
+        if (qrow >= N_q) qf[t] = bf16x8{};
+      }
+    }
+
+    // ---- which K/V tiles this block visits ----
+    int n_tiles = (N_k + BC - 1) / BC;
+    if (CAUSAL) {
+      const int max_key = min(q0 + kBR - 1, N_q - 1) + shift;
+      n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
+    }
+    const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;  // causal reach of this wave
+    const int row_lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1; // last key this row sees
+
+    // ---- carries ----
+    float m_run = kNegInf;  // reference max (log2 units of the scaled scores)
+    float l_run = 0.f;      // this lane's partial sum of p over its keys (fp32 p: for the LSE)
+    float lb_run = 0.f;     // the same sum over the bf16-rounded p the PV product uses (for O)
+    f32x16 o[T::NCB];
 #pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
-            kf[(t + 1) & 1][kb] =
-                *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[t + 1]);
-        }
+    for (int cb = 0; cb < T::NCB; ++cb) o[cb] = f32x16{};
+
+    // ---- K/V staging: global -> LDS directly (16-byte buffer loads with an LDS target) ----
+    // Wave w's DMA i fills rows ROWS_PER_DMA * (DMA * w + i) + lane / CHUNKS; the lane fetches
+    // the logical chunk that belongs at its position.  The descriptor starts at the tile and
+    // ends at N_k: rows past the end of the sequence arrive as zeros (K: scores that get
+    // masked; V: 0 * V = 0).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t dma_off[T::DMA];
 #pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+    for (int i = 0; i < T::DMA; ++i) {
+      const int r = T::ROWS_PER_DMA * (T::DMA * wave + i) + lane / T::CHUNKS;
+      const int pos = lane % T::CHUNKS;
+      dma_off[i] = (uint32_t)(r * D + 8 * (pos ^ T::swz(r))) * 2u;
+    }
+    // DMA i (0 .. 2*DMA-1) of tile j: the K rows first, then the V rows.  Past the end of the
+    // sequence the descriptor is empty and the stage receives zeros.
+    auto tile_rsrc = [&](const __bf16* base, int j) {
+      const int kbase = j * BC;
+      return make_rsrc(base + (size_t)kbase * D, range_bytes((long long)N_k - kbase, D * 2));
+    };
+    auto dma = [&](int i, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, __bf16* ks, __bf16* vs) {
+      const int ii = i % T::DMA;
+      const int dst = (T::DMA * wave_u + ii) * 512;
+      if (i < T::DMA) buffer_load16_lds(kr, dma_off[ii], ks + dst);
+      else buffer_load16_lds(vr, dma_off[ii], vs + dst);
+    };
+    // LDS read offsets (elements) of this lane's MFMA operands in a stage.  K fragment of
+    // 32-key block kb, k-step t: row kb*32 + l32, logical chunk 2t + hh.  V^T fragment of
+    // column block cb, key step u, half r: lane (16-group g16, index i16) points at key
+    // 16u + 8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.  The swizzle of a
+    // row depends only on its index mod 16, so kb and u enter as plain immediates.
+    int koff[D / 16];
 #pragma unroll
-        for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
-          dma(i, kr_next, vr_next, ks_next, vs_next);
+    for (int t = 0; t < D / 16; ++t) koff[t] = l32 * D + 8 * ((2 * t + hh) ^ T::swz(l32));
+    int voff[2][T::NCB];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int cb = 0; cb < T::NCB; ++cb) {
+        const int row = 8 * r + 4 * hh + (i16 >> 2);
+        const int c = 4 * cb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        voff[r][cb] = row * D + 8 * (c ^ T::swz(row)) + 4 * (i16 & 1);
       }
 
-      __builtin_amdgcn_s_setprio(0);
-      // ---- mask: ragged tail and the bottom-right causal edge ----
-      const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
-      if (need_mask) {
-        const int thr = row_lim - kbase - 4 * hh;  // key offset in this lane's numbering
+    if (n_tiles > 0) {
+      const auto kr = tile_rsrc(Kp, 0), vr = tile_rsrc(Vp, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * T::DMA; ++i) dma(i, kr, vr, Ks0, Vs0);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    // Tile j reads stage (ks, vs) while tile j+1 streams into (ks_next, vs_next), which
+    // tile j-1 read before the last barrier.
+    auto tile_step = [&](int j, const __bf16* ks, const __bf16* vs, __bf16* ks_next, __bf16* vs_next) {
+      // Tile j+1 streams into (ks_next, vs_next), which tile j-1 read before the last
+      // barrier.  Its DMAs are issued a few at a time between the score MFMAs: a wave that
+      // issued them all at once would sit at the first one whose queue slot is not free.
+      // (After the last tile the descriptors are empty: the stage gets zeros nobody reads.)
+      const auto kr_next = tile_rsrc(Kp, j + 1), vr_next = tile_rsrc(Vp, j + 1);
+      constexpr int NDMA = 2 * T::DMA;
+      constexpr int DMA_PER_STEP = (NDMA + D / 16 - 1) / (D / 16);
+      const int kbase = j * BC;
+
+      if (!CAUSAL || kbase <= wave_last_key) {
+        // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
+        __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
+        f32x16 s[T::NKB];
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
+        bf16x8 kf[2][T::NKB];
+#pragma unroll
+        for (int kb = 0; kb < T::NKB; ++kb)
+          kf[0][kb] = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[0]);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          if (t + 1 < D / 16) {
+#pragma unroll
+            for (int kb = 0; kb < T::NKB; ++kb)
+              kf[(t + 1) & 1][kb] =
+                  *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[t + 1]);
+          }
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+#pragma unroll
+          for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
+            dma(i, kr_next, vr_next, ks_next, vs_next);
+        }
+
+        __builtin_amdgcn_s_setprio(0);
+        // ---- mask: ragged tail and the bottom-right causal edge ----
+        const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
+        if (need_mask) {
+          const int thr = row_lim - kbase - 4 * hh;  // key offset in this lane's numbering
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) > thr) s[kb][r] = kNegInf;
+        }
+
+        // ---- online softmax (base 2, lazily rescaled) ----
+        float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) > thr) s[kb][r] = kNegInf;
-      }
-
-      // ---- online softmax (base 2, lazily rescaled) ----
-      float mx = kNegInf;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = max_halves(mx) * scale_log2;
+        if (wave_any(mx > m_run + kRescaleSlack)) {
+          const float m_new = fmaxf(m_run, mx);
+          // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
+          const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run - m_new);
+          l_run *= alpha;
+          lb_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = max_halves(mx) * scale_log2;
-      if (wave_any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
-        const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run - m_new);
-        l_run *= alpha;
-        lb_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) o[cb] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == kNegInf ? 0.f : m_run;  // a row with no key yet: all p = 0
-#pragma unroll
-      for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-          l_run += s[kb][r];
+          for (int cb = 0; cb < T::NCB; ++cb) o[cb] *= alpha;
+          m_run = m_new;
         }
-      // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
-      bf16x8 pf[BC / 16];
+        const float m_use = m_run == kNegInf ? 0.f : m_run;  // a row with no key yet: all p = 0
 #pragma unroll
-      for (int u = 0; u < BC / 16; ++u) {
-        const f32x16& sk = s[u >> 1];
-        const int r0 = (u & 1) * 8;
-        pf[u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
-                                sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
-        lb_run = sum_bf16x8(pf[u], lb_run);
-      }
-
-      // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
-      auto vfrag = [&](int u, int cb) {
-        const __bf16* p = vs + 16 * u * D;
-        return join_bf16x8(lds_read_tr16(p + voff[0][cb]), lds_read_tr16(p + voff[1][cb]));
-      };
-      bf16x8 vf[2][T::NCB];
+        for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < T::NCB; ++cb) vf[0][cb] = vfrag(0, cb);
-      __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
+          for (int r = 0; r < 16; ++r) {
+            s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+            l_run += s[kb][r];
+          }
+        // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
+        bf16x8 pf[BC / 16];
 #pragma unroll
-      for (int u = 0; u < BC / 16; ++u) {
-        if (u + 1 < BC / 16) {
-#pragma unroll
-          for (int cb = 0; cb < T::NCB; ++cb) vf[(u + 1) & 1][cb] = vfrag(u + 1, cb);
+        for (int u = 0; u < BC / 16; ++u) {
+          const f32x16& sk = s[u >> 1];
+          const int r0 = (u & 1) * 8;
+          pf[u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
+                                  sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
+          lb_run = sum_bf16x8(pf[u], lb_run);
         }
-#pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NDMA; ++i) dma(i, kr_next, vr_next, ks_next, vs_next);
-    }
-    wait_vmem();      // this wave's DMAs of tile j+1 have landed
-    __syncthreads();  // everyone's have; stage (ks, vs) is free for tile j+2
-  };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile_step(j, Ks0, Vs0, Ks1, Vs1);
-    if (j + 1 < n_tiles) tile_step(j + 1, Ks1, Vs1, Ks0, Vs0);
-  }
 
-  // ---- epilogue: one division, O and LSE written once ----
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);  // the two wave halves hold one row's keys
-  const float lb_tot = lb_run + shfl_xor_f(lb_run, 32);
-  if (qrow >= N_q) return;
-  const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
-  OutT* Orow = O + ((size_t)bh * N_q + qrow) * D;
+        // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
+        auto vfrag = [&](int u, int cb) {
+          const __bf16* p = vs + 16 * u * D;
+          return join_bf16x8(lds_read_tr16(p + voff[0][cb]), lds_read_tr16(p + voff[1][cb]));
+        };
+        bf16x8 vf[2][T::NCB];
 #pragma unroll
-  for (int cb = 0; cb < T::NCB; ++cb)
+        for (int cb = 0; cb < T::NCB; ++cb) vf[0][cb] = vfrag(0, cb);
+        __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = cb * 32 + 8 * g + 4 * hh;
-      const f32x4 v = {o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv,
-                       o[cb][4 * g + 3] * inv};
-      if constexpr (sizeof(OutT) == 4) {
-        *reinterpret_cast<f32x4*>(Orow + c) = v;
+        for (int u = 0; u < BC / 16; ++u) {
+          if (u + 1 < BC / 16) {
+#pragma unroll
+            for (int cb = 0; cb < T::NCB; ++cb) vf[(u + 1) & 1][cb] = vfrag(u + 1, cb);
+          }
+#pragma unroll
+          for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
+        }
+        __builtin_amdgcn_s_setprio(0);
       } else {
-        *reinterpret_cast<bf16x4*>(Orow + c) = __builtin_convertvector(v, bf16x4);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) dma(i, kr_next, vr_next, ks_next, vs_next);
       }
+      wait_vmem();      // this wave's DMAs of tile j+1 have landed
+      __syncthreads();  // everyone's have; stage (ks, vs) is free for tile j+2
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+      tile_step(j, Ks0, Vs0, Ks1, Vs1);
+      if (j + 1 < n_tiles) tile_step(j + 1, Ks1, Vs1, Ks0, Vs0);
     }
-  if (LSE != nullptr && hh == 0) {
-    LSE[(size_t)bh * N_q + qrow] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+
+    // ---- epilogue: one division, O and LSE written once ----
+    const float l_tot = l_run + shfl_xor_f(l_run, 32);  // the two wave halves hold one row's keys
+    const float lb_tot = lb_run + shfl_xor_f(lb_run, 32);
+    if (qrow < N_q) {
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+    OutT* Orow = O + ((size_t)bh * N_q + qrow) * D;
+#pragma unroll
+    for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = cb * 32 + 8 * g + 4 * hh;
+        const f32x4 v = {o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv,
+                         o[cb][4 * g + 3] * inv};
+        if constexpr (sizeof(OutT) == 4) {
+          *reinterpret_cast<f32x4*>(Orow + c) = v;
+        } else {
+          *reinterpret_cast<bf16x4*>(Orow + c) = __builtin_convertvector(v, bf16x4);
+        }
+      }
+    if (LSE != nullptr && hh == 0) {
+      LSE[(size_t)bh * N_q + qrow] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+    }
+    }
   }
 }
 
 template <int D, int BC, bool CAUSAL, typename OutT>
 static hipError_t launch(const FwdArgs& a) {
   const int n_qblocks = (a.N_q + kBR - 1) / kBR;
-  const long long total = (long long)a.B * a.H_q * n_qblocks;
+  const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
+  const long long total = (long long)a.B * a.H_q * n_units;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, CAUSAL, OutT>), dim3((unsigned)total), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (OutT*)a.O, a.LSE, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e, n_qblocks,
-                     (int)total);
+                     n_units, (int)total);
   return hipGetLastError();
 }
 
