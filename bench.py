@@ -10,9 +10,10 @@ causal).  ``roofline`` prices the dominant kernel's average launch (HIP events r
 the stream the library launches on) against the dense bf16 MFMA peak (prefill) or the
 HBM peak (decode), with ``traffic`` taken from the committed rocprofv3 counter summary
 when it was measured on the current kernel source.  ``breakdown`` adds the other
-prefill variants, the long causal prefill and the two decode workloads (decode timed
-with L2 and the Infinity Cache flushed by a 1 GiB read before every call).  ``cpu_baseline`` times the
-fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
+prefill variants, the long causal prefill, the chunked prefill over a paged cache (FLOPs:
+4 d per visible query-key pair, exact) and the two decode workloads (decode timed with L2
+and the Infinity Cache flushed by a 1 GiB read before every call).  ``cpu_baseline`` times
+the fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
 
 ``--workload`` makes another workload the timed one (for profiling); ``--calib-copy``
 adds a plain 1 GiB device copy (torch's copy kernel), the reference that scales the
@@ -35,7 +36,8 @@ PREFILL = {
     "prefill_d64_causal": (64, True), "prefill_d64_full": (64, False),
 }
 DECODE = ("decode_splitkv_128k", "decode_paged_b64")
-WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + DECODE
+PAGED_PREFILL = ("chunked_prefill_paged",)
+WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + PAGED_PREFILL + DECODE
 
 
 def parse():
@@ -99,6 +101,8 @@ def main():
             return workloads.prefill_4x16x4096(*PREFILL[name])
         if name == "long_prefill_8192":
             return workloads.long_prefill_8192()
+        if name == "chunked_prefill_paged":
+            return workloads.chunked_prefill_paged()
         if name == "decode_splitkv_128k":
             return workloads.decode_splitkv_128k()
         return workloads.decode_paged_b64()
@@ -113,6 +117,22 @@ def main():
         def fn():
             fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
         return fn, flops, (q, k, v, o, lse)
+
+    def paged_prefill_case(w):
+        q, k, v, bt = (t.to(dev) for t in (w.q, w.k, w.v, w.block_table))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        s = w.shape
+        flops = rl.chunked_prefill_flops(s["B"], s["H_q"], s["T"], s["N_k"], s["d"], w.causal)
+        assert 0 <= int(bt.min()) and int(bt.max()) < w.k.shape[0]   # once, outside any timing
+
+        def fn():
+            fa.fa_fwd_paged(q, k, v, bt, w.n_k, o, lse, causal=w.causal, scale=w.scale, check_table=False,
+                            stream=stream)
+        return fn, flops, (q, k, v, bt, o, lse)
+
+    def any_prefill_case(w):
+        return paged_prefill_case(w) if w.name.startswith("chunked_prefill") else prefill_case(w)
 
     def decode_case(w, ns):
         q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
@@ -157,14 +177,20 @@ def main():
             s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"]), "bytes_per_step": nbytes,
             "paged": w.block_table is not None}
     else:
-        fn, flops, bufs = prefill_case(w)
+        paged = head in PAGED_PREFILL
+        fn, flops, bufs = any_prefill_case(w)
         total_ms, per = timed(fn, args.steps, args.warmup)
         avg = statistics.mean(per)
         ms_per_step = total_ms / args.steps
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit, bound, peak, achieved = "TFLOP/s", "mfma", rl.PEAK_BF16_MFMA_TFLOPS, flops / (avg * 1e-3) / 1e12
-        kernel = f"fa::fwd_bf16_kernel<{s['d']}, {64 if s['d'] == 128 else 128}, {str(w.causal).lower()}, bf16>"
-        extra_cfg = {"N_q": s["N_q"], "N_k": s["N_k"], "causal": w.causal, "flops_per_step": flops}
+        kernel = (f"fa::fwd_bf16_kernel<{s['d']}, {64 if s['d'] == 128 else 128}, {str(w.causal).lower()}, "
+                  f"{str(paged).lower()}, bf16>")
+        extra_cfg = {"N_q": s["T"] if paged else s["N_q"], "N_k": s["N_k"], "causal": w.causal,
+                     "flops_per_step": flops}
+        if paged:
+            extra_cfg.update({"paged": True, "page_size": w.page_size,
+                              "flops": "4 d per visible (query, key) pair, exact"})
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -195,7 +221,7 @@ def main():
             if name == head or name in DECODE:
                 continue
             ww = make(name)
-            fn, fl, bufs = prefill_case(ww)
+            fn, fl, bufs = any_prefill_case(ww)
             _, per = timed(fn, max(10, args.steps // 2), 3)
             med = statistics.median(per)
             breakdown[ww.name] = {"us": round(med * 1e3, 2), "TFLOP/s": round(fl / med / 1e9, 2),
@@ -251,19 +277,33 @@ def cpu_baseline(w, rl):
     import oracle.fa_oracle as orc
     from threadpoolctl import threadpool_info
     q, k, v = (t.float().numpy() for t in (w.q, w.k, w.v))
+    paged = getattr(w, "block_table", None) is not None
     B, H = q.shape[:2]
     g = H // k.shape[1]
     heads = 0
     t0 = time.perf_counter()
+    if paged:   # the oracle's own gather, one sequence at a time, inside the timing
+        g = H // k.shape[2]
+    kb = None
     for bh in range(B * H):
         b, h = divmod(bh, H)
-        orc.attention_head(q[b, h], k[b, h // g], v[b, h // g], w.scale, w.causal)
+        if paged:
+            if h == 0:
+                bt = w.block_table.numpy()[b:b + 1]
+                kb = orc.gather_pages(k, bt, w.n_k, w.page_size)[0]
+                vb = orc.gather_pages(v, bt, w.n_k, w.page_size)[0]
+            orc.attention_head(q[b, h], kb[h // g], vb[h // g], w.scale, w.causal)
+        else:
+            orc.attention_head(q[b, h], k[b, h // g], v[b, h // g], w.scale, w.causal)
         heads += 1
         if time.perf_counter() - t0 > 10.0:
             break
     el = time.perf_counter() - t0
     s = w.shape
-    fl = rl.prefill_flops(1, heads, s["N_q"], s["N_k"], s["d"], w.causal)
+    if paged:
+        fl = rl.chunked_prefill_flops(1, heads, s["T"], s["N_k"], s["d"], w.causal)
+    else:
+        fl = rl.prefill_flops(1, heads, s["N_q"], s["N_k"], s["d"], w.causal)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s",
             "cores": min(threads, len(os.sched_getaffinity(0))), "kind": "oracle",

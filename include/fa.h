@@ -12,7 +12,7 @@
  * batch*head*N*D):
  *   Q, O            [B, H_q,  N_q, d]          (decode: N_q = T new queries)
  *   K, V            [B, H_kv, N_k, d]          (contiguous cache)
- *   K, V pools      [num_pages, page_size, H_kv, d]   (paged cache, decode only)
+ *   K, V pools      [num_pages, page_size, H_kv, d]   (paged cache: fa_fwd_paged, decode)
  *   LSE             [B, H_q, N_q] fp32
  *   block_table     [B, pages_per_seq] int32
  *
@@ -76,6 +76,30 @@ typedef enum fa_dtype {
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H_q, int H_kv, int N_q, int N_k, int d,
            float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_paged -- fa_fwd over a paged KV cache: chunked prefill, where the N_q new tokens
+ * of each sequence attend to the N_k cached ones (the last N_q of which are usually those
+ * same new tokens), read through a block table.
+ *
+ * Defined by: the same passages as fa_fwd for the arithmetic and loop order; page
+ * "Attention kernel chains", chain "The block-table cost of paged attention" (one int32
+ * page index per page_size-token block) for the key addressing, and chain "The causal mask
+ * for a decode step" for the mask: with N_q < N_k the queries are the LAST N_q positions,
+ * so query i sees keys j <= i + N_k - N_q.
+ *
+ *   Q [B,H_q,N_q,d] bf16; O [B,H_q,N_q,d] bf16 (FA_BF16) or fp32 (FA_BF16_IN_FP32_OUT);
+ *   LSE [B,H_q,N_q] fp32 (may be NULL).
+ *   K/V pools [num_pages,page_size,H_kv,d] bf16 (the layout fa_decode_splitkv reads): key j
+ *     of sequence b is slot j%page_size of page block_table[b*pages_per_seq + j/page_size].
+ *   page_size >= 1, pages_per_seq*page_size >= N_k, N_k < 2^24.  Table contents are not
+ *     checked: an entry outside the pool is undefined behaviour, as in any gather.
+ *   d in {64, 128}.  scale > 0.  causal: 0 or 1 (bottom-right).  stream: hipStream_t or NULL.
+ */
+int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+                 const int32_t* block_table, int page_size, int pages_per_seq,
+                 int dtype, void* stream);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode_splitkv uses when called with

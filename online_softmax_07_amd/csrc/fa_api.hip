@@ -59,7 +59,7 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 101; }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
            int N_q, int N_k, int d, float scale, int causal, int dtype, void* stream) {
@@ -74,6 +74,24 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
   if (dtype == FA_FP32) return status_of(fa::launch_fwd_fp32(a));
   return status_of(fa::launch_fwd_bf16(a, dtype == FA_BF16_IN_FP32_OUT));
+}
+
+int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
+                 int N_q, int N_k, int d, float scale, int causal, const int32_t* block_table, int page_size,
+                 int pages_per_seq, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !block_table) return FA_ERR_NULL_PTR;
+  int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
+  if (st != FA_OK) return st;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
+  if (page_size < 1 || pages_per_seq < 1 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
+  if ((long long)B * pages_per_seq > 0x7fffffffLL || N_k >= (1 << 24)) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)) ||
+      !aligned4(block_table))
+    return FA_ERR_ALIGNMENT;
+  fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
+  return status_of(fa::launch_fwd_bf16_paged(a, dtype == FA_BF16_IN_FP32_OUT, block_table, page_size, pages_per_seq));
 }
 
 int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d) {

@@ -121,6 +121,13 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
                                            (int)voffset, 0, 0, 0);
 }
 
+// 16 bytes per lane from a global address straight into LDS: lane L of the wave writes
+// lds_wave_base + 16 L bytes (lds_wave_base must be wave-uniform); no range check.
+__device__ __forceinline__ void global_load16_lds(const void* src, __bf16* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)const_cast<void*>(src),
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 // s_waitcnt vmcnt(0): every vector-memory load of this wave (LDS DMAs included) has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

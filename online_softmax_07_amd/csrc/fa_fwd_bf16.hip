@@ -63,11 +63,12 @@ struct FwdTile {
   }
 };
 
-template <int D, int BC, bool CAUSAL, typename OutT>
+template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
-    float scale_log2, int n_qblocks, int n_units, int total_wg) {
+    float scale_log2, int n_qblocks, int n_units, int total_wg,
+    const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, float inv_page_size) {
   using T = FwdTile<D, BC>;
   // Two K and two V stages as separate arrays: with the stage known at compile time the
   // compiler can tell that a tile's LDS reads do not touch the stage being refilled, and
@@ -100,8 +101,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int h = bh - b * H_q;
   const int hk = h / (H_q / H_kv);
   const __bf16* Qp = Q + (size_t)bh * N_q * D;
-  const __bf16* Kp = K + ((size_t)b * H_kv + hk) * N_k * D;
-  const __bf16* Vp = V + ((size_t)b * H_kv + hk) * N_k * D;
+  // contiguous K/V: this head's rows; paged: the pools (rows found through the table)
+  const __bf16* Kp = PAGED ? K : K + ((size_t)b * H_kv + hk) * N_k * D;
+  const __bf16* Vp = PAGED ? V : V + ((size_t)b * H_kv + hk) * N_k * D;
+  const int32_t* table_b = PAGED ? block_table + (size_t)b * pages_per_seq : nullptr;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -159,18 +162,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       const int pos = lane % T::CHUNKS;
       dma_off[i] = (uint32_t)(r * D + 8 * (pos ^ T::swz(r))) * 2u;
     }
-    // DMA i (0 .. 2*DMA-1) of tile j: the K rows first, then the V rows.  Past the end of the
-    // sequence the descriptor is empty and the stage receives zeros.
+    // DMA i (0 .. 2*DMA-1) of tile j: the K rows first, then the V rows.  Contiguous K/V:
+    // buffer loads whose descriptor starts at the tile and ends at N_k, so rows past the end
+    // of the sequence arrive as zeros.  Paged K/V (page "Attention kernel chains", chain
+    // "The block-table cost of paged attention"): key j of sequence b is slot j % page_size
+    // of pool page block_table[b][j / page_size]; each lane loads its row from its own
+    // address, keys past the end are clamped to the last key (masked like any other), and
+    // the table entries of a tile are read two tiles ahead so the dependent load is never
+    // waited for.
     auto tile_rsrc = [&](const __bf16* base, int j) {
       const int kbase = j * BC;
       return make_rsrc(base + (size_t)kbase * D, range_bytes((long long)N_k - kbase, D * 2));
     };
-    auto dma = [&](int i, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, __bf16* ks, __bf16* vs) {
-      const int ii = i % T::DMA;
-      const int dst = (T::DMA * wave_u + ii) * 512;
-      if (i < T::DMA) buffer_load16_lds(kr, dma_off[ii], ks + dst);
-      else buffer_load16_lds(vr, dma_off[ii], vs + dst);
+    int dma_row[T::DMA];        // paged: tile row of this lane's DMA i
+    uint32_t dma_chunk[T::DMA]; // paged: byte offset of its 16-byte chunk within the row
+#pragma unroll
+    for (int i = 0; i < T::DMA; ++i) {
+      dma_row[i] = T::ROWS_PER_DMA * (T::DMA * wave + i) + lane / T::CHUNKS;
+      dma_chunk[i] = (uint32_t)(16 * ((lane % T::CHUNKS) ^ T::swz(dma_row[i])));
+    }
+    auto key_page = [&](int key) {  // key / page_size, exact for key < 2^24
+      int q = (int)((float)key * inv_page_size);
+      q -= q * page_size > key ? 1 : 0;
+      q += (q + 1) * page_size <= key ? 1 : 0;
+      return q;
     };
+    auto read_pages = [&](int j, int (&pg)[T::DMA]) {
+#pragma unroll
+      for (int i = 0; i < T::DMA; ++i) pg[i] = table_b[key_page(min(j * BC + dma_row[i], N_k - 1))];
+    };
+    auto pool_offset = [&](int j, const int (&pg)[T::DMA], int i) {  // bytes
+      const int key = min(j * BC + dma_row[i], N_k - 1);
+      const long long prow = (long long)pg[i] * page_size + (key - key_page(key) * page_size);
+      return (size_t)(prow * H_kv + hk) * (D * 2) + dma_chunk[i];
+    };
+    auto dma = [&](int i, int j, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, const int (&pg)[T::DMA],
+                   __bf16* ks, __bf16* vs) {
+      const int ii = i % T::DMA;
+      __bf16* dst = (i < T::DMA ? ks : vs) + (T::DMA * wave_u + ii) * 512;
+      if constexpr (PAGED) {
+        const char* src = reinterpret_cast<const char*>(i < T::DMA ? Kp : Vp) + pool_offset(j, pg, ii);
+        global_load16_lds(src, dst);
+      } else {
+        buffer_load16_lds(i < T::DMA ? kr : vr, dma_off[ii], dst);
+      }
+    };
+    int pg_next[T::DMA], pg_after[T::DMA];  // paged: pages of tiles j+1 and j+2
     // LDS read offsets (elements) of this lane's MFMA operands in a stage.  K fragment of
     // 32-key block kb, k-step t: row kb*32 + l32, logical chunk 2t + hh.  V^T fragment of
     // column block cb, key step u, half r: lane (16-group g16, index i16) points at key
@@ -191,8 +228,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     if (n_tiles > 0) {
       const auto kr = tile_rsrc(Kp, 0), vr = tile_rsrc(Vp, 0);
+      if constexpr (PAGED) {
+        read_pages(0, pg_next);
+        read_pages(1, pg_after);
+      }
 #pragma unroll
-      for (int i = 0; i < 2 * T::DMA; ++i) dma(i, kr, vr, Ks0, Vs0);
+      for (int i = 0; i < 2 * T::DMA; ++i) dma(i, 0, kr, vr, pg_next, Ks0, Vs0);
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < T::DMA; ++i) pg_next[i] = pg_after[i];
+      }
     }
     wait_vmem();
     __syncthreads();
@@ -205,6 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
       // issued them all at once would sit at the first one whose queue slot is not free.
       // (After the last tile the descriptors are empty: the stage gets zeros nobody reads.)
       const auto kr_next = tile_rsrc(Kp, j + 1), vr_next = tile_rsrc(Vp, j + 1);
+      if constexpr (PAGED) read_pages(j + 2, pg_after);  // lands during this tile
       constexpr int NDMA = 2 * T::DMA;
       constexpr int DMA_PER_STEP = (NDMA + D / 16 - 1) / (D / 16);
       const int kbase = j * BC;
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
 #pragma unroll
           for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
-            dma(i, kr_next, vr_next, ks_next, vs_next);
+            dma(i, j + 1, kr_next, vr_next, pg_next, ks_next, vs_next);
         }
 
         __builtin_amdgcn_s_setprio(0);
@@ -303,7 +349,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(0);
       } else {
 #pragma unroll
-        for (int i = 0; i < NDMA; ++i) dma(i, kr_next, vr_next, ks_next, vs_next);
+        for (int i = 0; i < NDMA; ++i) dma(i, j + 1, kr_next, vr_next, pg_next, ks_next, vs_next);
+      }
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < T::DMA; ++i) pg_next[i] = pg_after[i];
       }
       wait_vmem();      // this wave's DMAs of tile j+1 have landed
       __syncthreads();  // everyone's have; stage (ks, vs) is free for tile j+2
@@ -339,28 +389,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int BC, bool CAUSAL, typename OutT>
-static hipError_t launch(const FwdArgs& a) {
+template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
+static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_size, int pages_per_seq) {
   const int n_qblocks = (a.N_q + kBR - 1) / kBR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
   const long long total = (long long)a.B * a.H_q * n_units;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, CAUSAL, OutT>), dim3((unsigned)total), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, CAUSAL, PAGED, OutT>), dim3((unsigned)total), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (OutT*)a.O, a.LSE, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e, n_qblocks,
-                     n_units, (int)total);
+                     n_units, (int)total, block_table, page_size, pages_per_seq,
+                     page_size > 0 ? 1.f / (float)page_size : 0.f);
   return hipGetLastError();
 }
 
-template <int D, int BC>
-static hipError_t dispatch_out(const FwdArgs& a, bool out_f32) {
-  if (a.causal) return out_f32 ? launch<D, BC, true, float>(a) : launch<D, BC, true, __bf16>(a);
-  return out_f32 ? launch<D, BC, false, float>(a) : launch<D, BC, false, __bf16>(a);
+template <int D, int BC, bool PAGED>
+static hipError_t dispatch_out(const FwdArgs& a, bool out_f32, const int32_t* bt, int ps, int pps) {
+  if (a.causal)
+    return out_f32 ? launch<D, BC, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC, true, PAGED, __bf16>(a, bt, ps, pps);
+  return out_f32 ? launch<D, BC, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC, false, PAGED, __bf16>(a, bt, ps, pps);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32) {
-  if (a.d == 128) return dispatch_out<128, 64>(a, out_f32);
-  return dispatch_out<64, 128>(a, out_f32);
+  if (a.d == 128) return dispatch_out<128, 64, false>(a, out_f32, nullptr, 0, 0);
+  return dispatch_out<64, 128, false>(a, out_f32, nullptr, 0, 0);
+}
+
+hipError_t launch_fwd_bf16_paged(const FwdArgs& a, bool out_f32, const int32_t* block_table, int page_size,
+                                 int pages_per_seq) {
+  if (a.d == 128) return dispatch_out<128, 64, true>(a, out_f32, block_table, page_size, pages_per_seq);
+  return dispatch_out<64, 128, true>(a, out_f32, block_table, page_size, pages_per_seq);
 }
 
 }  // namespace fa

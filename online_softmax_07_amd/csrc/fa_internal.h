@@ -40,6 +40,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32);
+hipError_t launch_fwd_bf16_paged(const FwdArgs& a, bool out_f32, const int32_t* block_table, int page_size,
+                                 int pages_per_seq);
 hipError_t launch_fwd_fp32(const FwdArgs& a);
 hipError_t launch_decode_split(const DecodeArgs& a, bool out_f32);
 hipError_t launch_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE,

@@ -23,7 +23,7 @@ from . import build as _build
 FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_ALIGNMENT, FA_ERR_HIP = range(7)
 FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
 
-EXPORTED = ("fa_fwd", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
             "fa_lse_merge", "fa_status_string", "fa_version")
 
 _lib = None
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.fa_fwd.restype = i
+    L.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp]
+    L.fa_fwd_paged.restype = i
     L.fa_decode_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_decode_num_splits.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -146,6 +148,59 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.
     return o, lse
 
 
+def _paged_sizes(q, k, block_table, n_k, check_table):
+    """(H_kv, N_k, page_size, pages_per_seq) of a paged cache: k is a pool
+    [num_pages, page_size, H_kv, d], block_table int32 [B, pages_per_seq]."""
+    B, d = q.shape[0], q.shape[3]
+    num_pages, page_size, H_kv, dk = k.shape
+    _need(dk == d, "pool head dimension must match q")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
+          "block_table must be int32 [B, pages_per_seq]")
+    _need(block_table.is_contiguous(), "block_table must be contiguous")
+    pages_per_seq = block_table.shape[1]
+    N_k = pages_per_seq * page_size if n_k is None else int(n_k)
+    _need(1 <= N_k <= pages_per_seq * page_size, "n_k exceeds the block table")
+    _check_dev(q.device, block_table=block_table)
+    if check_table:
+        lo, hi = int(block_table.min()), int(block_table.max())
+        _need(0 <= lo and hi < num_pages, f"block_table entries must lie in [0, {num_pages})")
+    return H_kv, N_k, page_size, pages_per_seq
+
+
+def fa_fwd_paged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor,
+                 n_k: Optional[int] = None, o: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, *, causal: bool = True, scale: Optional[float] = None,
+                 out_dtype: Optional[torch.dtype] = None, want_lse: bool = True, check_table: bool = True,
+                 stream=None):
+    """Chunked prefill over a paged cache.  q [B,H_q,N_q,d] bf16 (the last N_q of the
+    ``n_k`` positions of each sequence); k, v pools [num_pages,page_size,H_kv,d] bf16;
+    block_table [B,pages_per_seq] int32; ``n_k`` defaults to pages_per_seq*page_size.
+    With ``check_table`` the table entries are checked to lie inside the pool."""
+    _need(q.dim() == 4 and q.dtype == torch.bfloat16, "q must be bf16 [B,H_q,N_q,d]")
+    B, H_q, N_q, d = q.shape
+    _need(k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and k.shape == v.shape and k.dim() == 4,
+          "k, v must be bf16 pools of the same shape")
+    H_kv, N_k, page_size, pages_per_seq = _paged_sizes(q, k, block_table, n_k, check_table)
+    odt = out_dtype or (o.dtype if o is not None else torch.bfloat16)
+    _need(odt in (torch.bfloat16, torch.float32), "output must be bf16 or fp32")
+    dtype = FA_BF16 if odt == torch.bfloat16 else FA_BF16_IN_FP32_OUT
+    if o is None:
+        o = torch.empty((B, H_q, N_q, d), dtype=odt, device=q.device)
+    _need(o.shape == (B, H_q, N_q, d) and o.dtype == odt, "o has the wrong shape or dtype")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse.shape == (B, H_q, N_q) and lse.dtype == torch.float32, "lse must be fp32 [B,H_q,N_q]")
+    _check_dev(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_paged(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H_q, H_kv, N_q, N_k, d,
+                            float(scale), int(bool(causal)), _ptr(block_table), int(page_size),
+                            int(pages_per_seq), dtype, _stream(stream, q.device))
+    _raise(st, "fa_fwd_paged")
+    return o, lse
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
@@ -178,17 +233,7 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Opti
         page_size = pages_per_seq = 0
         _need(n_k in (None, N_k), "n_k must equal k.shape[2] for a contiguous cache")
     else:
-        num_pages, page_size, H_kv, dk = k.shape
-        _need(dk == d, "pool head dimension must match q")
-        _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B,
-              "block_table must be int32 [B, pages_per_seq]")
-        pages_per_seq = block_table.shape[1]
-        N_k = pages_per_seq * page_size if n_k is None else int(n_k)
-        _need(1 <= N_k <= pages_per_seq * page_size, "n_k exceeds the block table")
-        _check_dev(q.device, block_table=block_table)
-        if check_table:
-            lo, hi = int(block_table.min()), int(block_table.max())
-            _need(0 <= lo and hi < num_pages, f"block_table entries must lie in [0, {num_pages})")
+        H_kv, N_k, page_size, pages_per_seq = _paged_sizes(q, k, block_table, n_k, check_table)
     odt = out_dtype or (o.dtype if o is not None else torch.bfloat16)
     _need(odt in (torch.bfloat16, torch.float32), "output must be bf16 or fp32")
     dtype = FA_BF16 if odt == torch.bfloat16 else FA_BF16_IN_FP32_OUT

@@ -27,6 +27,22 @@ def prefill_flops(B, H_q, N_q, N_k, d, causal) -> float:
     return f / 2 if causal else f
 
 
+def visible_pairs(N_q, N_k, causal) -> int:
+    """Exact count of (query, key) pairs a head computes: with the bottom-right mask,
+    query i sees max(0, i + N_k - N_q + 1) keys (never more than N_k)."""
+    if not causal:
+        return N_q * N_k
+    shift = N_k - N_q
+    lo = max(0, -shift)   # first query that sees a key
+    n = N_q - lo          # queries that see one
+    return n * (lo + shift + 1) + n * (n - 1) // 2
+
+
+def chunked_prefill_flops(B, H_q, N_q, N_k, d, causal) -> float:
+    """4 d FLOPs per visible (query, key) pair, counted exactly."""
+    return 4.0 * d * visible_pairs(N_q, N_k, causal) * B * H_q
+
+
 def prefill_bytes_floor(B, H_q, H_kv, N_q, N_k, d, e=2, lse=True) -> float:
     """Q and O once, K and V once per KV head, plus the fp32 LSE."""
     b = e * (2.0 * B * H_q * N_q * d + 2.0 * B * H_kv * N_k * d)

@@ -17,7 +17,10 @@ The shapes are the pages' workloads:
 * decode at batch 1, 8 KV heads, 128K context (Attention kernel chains, "How
   many splits for decode") and one GPU's share (H_q = 8, H_kv = 1) of a
   64-query-head / 8-KV-head model at batch 64, 8K context, 16-token pages
-  ("GQA loads KV once per group", "The block-table cost of paged attention").
+  ("GQA loads KV once per group", "The block-table cost of paged attention");
+* chunked prefill over the same kind of paged cache: the last 2048 of 8192 positions
+  of 4 sequences at 32 query / 8 KV heads (the decode model's head layout), 16-token
+  pages ("The causal mask for a decode step": the new queries sit at the end).
 
 N(0,1) values stand in for activations; no dataset is involved.
 """
@@ -156,6 +159,13 @@ def decode_splitkv_128k() -> Decode:
     """B=1, T=1, H_q=32, H_kv=8, d=128, S=131072 contiguous, causal (bottom-right)."""
     return decode(1, 32, 8, 1, 131072, 128, seed=400, causal=True,
                   num_splits=(1, 8, 16, 32, 64), name="decode_splitkv_b1_hq32_hkv8_s131072")
+
+
+def chunked_prefill_paged() -> Decode:
+    """B=4, H_q=32, H_kv=8, d=128: a 2048-token chunk over 8192 cached positions (the chunk's
+    own keys included), 16-token pages in a shuffled pool of 4*512 + 64 pages, causal."""
+    return decode(4, 32, 8, 2048, 8192, 128, seed=600, causal=True, page_size=16,
+                  num_pages=4 * 512 + 64, name="chunked_prefill_paged_b4_hq32_hkv8_q2048_ctx8192_p16")
 
 
 def decode_paged_b64() -> Decode:

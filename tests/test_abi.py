@@ -48,7 +48,7 @@ def test_build_is_current():
 
 def test_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_version() == 100
+    assert L.fa_version() == 101
     for s in range(7):
         assert fa.fa_status_string(s).startswith(
             ["FA_OK", "FA_ERR_NULL_PTR", "FA_ERR_BAD_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
@@ -78,6 +78,31 @@ def fwd(**kw):
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
+
+
+def fwd_paged(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=2, H_q=4, H_kv=2, N_q=16, N_k=100, d=128, scale=0.1, causal=1,
+             bt=P, ps=16, pps=7, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_fwd_paged(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H_q"], a["H_kv"],
+                                 a["N_q"], a["N_k"], a["d"], a["scale"], a["causal"], a["bt"], a["ps"],
+                                 a["pps"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(V=None), fa.FA_ERR_NULL_PTR), (dict(bt=None), fa.FA_ERR_NULL_PTR),
+    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE), (dict(causal=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(ps=0), fa.FA_ERR_BAD_SHAPE), (dict(pps=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(pps=6), fa.FA_ERR_BAD_SHAPE),                       # 6 * 16 < 100 keys
+    (dict(N_k=1 << 24, pps=1 << 20), fa.FA_ERR_BAD_SHAPE),    # beyond the exact page division
+    (dict(B=1 << 16, pps=1 << 16, N_k=16), fa.FA_ERR_BAD_SHAPE),  # table entries beyond int32
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(K=P + 8), fa.FA_ERR_ALIGNMENT), (dict(O=P + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(bt=P + 2), fa.FA_ERR_ALIGNMENT), (dict(LSE=P + 1), fa.FA_ERR_ALIGNMENT),
+])
+def test_fwd_paged_rejects(kw, status):
+    assert fwd_paged(**kw) == status
 
 
 def dec(**kw):

@@ -94,6 +94,8 @@ SMALL = [
     (2, 4, 2, 2, 101, 128, True, 5, 3),      # odd page size, ragged last page
     (1, 8, 8, 1, 1024, 64, True, 64, 0),
     (4, 8, 1, 1, 8192, 128, True, 16, 0),
+    (8, 32, 8, 4, 4096, 128, True, 16, 0),   # multi-token decode over pages: 16 stacked rows
+    (2, 8, 1, 16, 2000, 64, True, 16, 0),    # 128 stacked rows, ragged last page
 ]
 
 
