@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the FlashAttention forward pass and split-KV decode.
+"""fp64 CPU oracle for the FlashAttention forward and backward passes and split-KV decode.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no
@@ -25,7 +25,10 @@ be checked by eye against the pages:
 * paged KV: token j of sequence b lives in pool page block_table[b, j // P],
   slot j % P  (Attention kernel chains, "The block-table cost of paged attention");
 * the LSE merge of normalized partials: lse = ln sum_s e^{lse_s},
-  O = sum_s e^{lse_s - lse} O_s  (Attention kernel chains, "The log-sum-exp merge").
+  O = sum_s e^{lse_s - lse} O_s  (Attention kernel chains, "The log-sum-exp merge");
+* the backward pass: dQ, dK, dV for an upstream gradient dO, with the extra row
+  vector D = rowsum(dO * O)  (Attention kernel chains, "What the backward pass
+  saves"); the other steps are the chain rule of the definition above.
 
 The two online recurrences at the bottom (``online_softmax_fa2`` and
 ``online_softmax_fa1``) follow the steps of the pages' derivation in the pages'
@@ -265,6 +268,81 @@ def lse_merge(O_parts: np.ndarray, lse_parts: np.ndarray):
     w = np.where(seen[None], np.exp(lse_parts - lse_safe[None]), 0.0)   # e^{lse_s - lse}
     O = np.sum(w[..., None] * O_parts, axis=0)
     return O, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+
+def attention_head_backward(q, k, v, do, scale: float, causal: bool, row_chunk: int = 512):
+    """Gradients dQ [n_q, d], dK [n_k, d], dV [n_k, d] of one head, in fp64, for the
+    upstream gradient dO [n_q, d] of O = softmax(scale * q K^T, masked) V.
+
+    Attention kernel chains, "What the backward pass saves": the backward keeps Q, K,
+    V, O and the per-row LSE, rebuilds P from them, and needs one extra vector per
+    row, D = rowsum(dO * O).  The pages give no more of it; the remaining steps are
+    the chain rule of the forward definition, written out:
+
+        P   = the masked safe softmax of the score row (zeros for a row with no key)
+        O   = P V,                 D_i = sum_c dO[i,c] O[i,c]
+        dV  = P^T dO               (O is linear in V)
+        dP  = dO V^T
+        dS  = P * (dP - D)         (softmax Jacobian: dS_ij = P_ij (dP_ij - sum_t P_it dP_it))
+        dQ  = scale dS K,          dK = scale dS^T q
+
+    Rows are taken ``row_chunk`` at a time only to bound memory; dK and dV are the
+    sums of the chunks' contributions.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n_q, n_k = q.shape[0], k.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n_q, row_chunk):
+        r = np.arange(r0, min(n_q, r0 + row_chunk))
+        x = scale * (q[r] @ k.T)
+        x = np.where(visible_mask(n_q, n_k, causal, rows=r), x, NEG_INF)
+        m = np.max(x, axis=1, keepdims=True)
+        m_safe = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(x - m_safe)
+        l = np.sum(e, axis=1, keepdims=True)
+        p = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
+        o = p @ v
+        D = np.sum(do[r] * o, axis=1)
+        dv += p.T @ do[r]
+        dp = do[r] @ v.T
+        ds = p * (dp - D[:, None])
+        dq[r] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r])
+    return dq, dk, dv
+
+
+def attention_backward(Q, K, V, dO, scale: float, causal: bool, heads=None):
+    """dQ [B, H_q, N_q, d], dK and dV [B, H_kv, N_k, d] in fp64.
+
+    GQA (Attention kernel chains, "GQA loads KV once per group"): query head h reads
+    KV head h // g, so the gradient of KV head hk is the sum over the g query heads
+    of its group.  ``heads`` (optional): a list of (b, hk) KV heads to compute; the
+    other entries stay zero (sampled checks at full size).
+    """
+    B, H_q, N_q, d = Q.shape
+    _, H_kv, N_k, _ = K.shape
+    assert H_q % H_kv == 0, "H_q must be a multiple of H_kv"
+    g = H_q // H_kv
+    dQ = np.zeros(Q.shape, dtype=np.float64)
+    dK = np.zeros(K.shape, dtype=np.float64)
+    dV = np.zeros(V.shape, dtype=np.float64)
+    todo = [(b, hk) for b in range(B) for hk in range(H_kv)] if heads is None else heads
+    for b, hk in todo:
+        for h in range(hk * g, (hk + 1) * g):
+            dq, dk, dv = attention_head_backward(Q[b, h], K[b, hk], V[b, hk], dO[b, h], scale, causal)
+            dQ[b, h] = dq
+            dK[b, hk] += dk
+            dV[b, hk] += dv
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------

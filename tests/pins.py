@@ -301,9 +301,123 @@ def check_online_equals_two_pass(orc):
     assert worst <= 1e-14, worst
 
 
+# --- the backward pass -----------------------------------------------------------
+
+def _sdpa_grads(Q, K, V, dO, scale, causal):
+    """dQ, dK, dV by torch autograd through scaled_dot_product_attention in fp64 on the
+    CPU (explicit bottom-right mask; GQA by repeat_interleave, whose backward sums the
+    group)."""
+    Qt, Kt, Vt = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (Q, K, V))
+    g = Q.shape[1] // K.shape[1]
+    n_q, n_k = Q.shape[2], K.shape[2]
+    i = torch.arange(n_q)[:, None]
+    j = torch.arange(n_k)[None, :]
+    mask = (j <= i + (n_k - n_q)) if causal else torch.ones(n_q, n_k, dtype=torch.bool)
+    O = torch.nn.functional.scaled_dot_product_attention(
+        Qt, Kt.repeat_interleave(g, dim=1), Vt.repeat_interleave(g, dim=1), attn_mask=mask, scale=scale)
+    (O * torch.from_numpy(dO)).sum().backward()
+    return Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy()
+
+
+def check_backward_vs_autograd(orc):
+    rng = np.random.default_rng(21)
+    for (B, Hq, Hkv, n_q, n_k, d, causal) in [(2, 4, 2, 37, 53, 16, True), (1, 3, 3, 40, 40, 32, False),
+                                              (1, 8, 2, 5, 70, 8, True), (1, 2, 1, 33, 33, 8, True)]:
+        Q, dO = rng.standard_normal((B, Hq, n_q, d)), rng.standard_normal((B, Hq, n_q, d))
+        K, V = rng.standard_normal((B, Hkv, n_k, d)), rng.standard_normal((B, Hkv, n_k, d))
+        got = orc.attention_backward(Q, K, V, dO, 0.41, causal)
+        ref = _sdpa_grads(Q, K, V, dO, 0.41, causal)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            assert a.shape == b.shape and np.allclose(a, b, atol=1e-12), (name, np.abs(a - b).max())
+
+
+def check_backward_finite_differences(orc):
+    """Central differences of L = sum(O * dO), with O from torch's attention (not the
+    oracle), against every gradient entry: tiny causal GQA case with N_q < N_k."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, n_q, n_k, d, scale = 1, 2, 1, 4, 6, 3, 0.7
+    Q, dO = rng.standard_normal((B, Hq, n_q, d)), rng.standard_normal((B, Hq, n_q, d))
+    K, V = rng.standard_normal((B, Hkv, n_k, d)), rng.standard_normal((B, Hkv, n_k, d))
+
+    def loss(Q_, K_, V_):
+        return float(np.sum(_sdpa_reference(Q_, K_, V_, scale, True)[0] * dO))
+
+    got = orc.attention_backward(Q, K, V, dO, scale, True)
+    h = 1e-5
+    for which, (X, G) in enumerate(zip((Q, K, V), got)):
+        assert G.shape == X.shape
+        for idx in itertools.product(*(range(n) for n in X.shape)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            args_p[which], args_m[which] = Xp, Xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - G[idx]) <= 1e-7, ("dQ dK dV".split()[which], idx, fd, G[idx])
+
+
+def check_backward_closed_forms(orc):
+    rng = np.random.default_rng(23)
+    # one key: P = 1, so dV = sum of dO over the rows, and dQ = dK = 0
+    Q, dO = rng.standard_normal((1, 1, 7, 4)), rng.standard_normal((1, 1, 7, 4))
+    K, V = rng.standard_normal((1, 1, 1, 4)), rng.standard_normal((1, 1, 1, 4))
+    dQ, dK, dV = orc.attention_backward(Q, K, V, dO, 0.5, False)
+    assert np.allclose(dQ, 0, atol=1e-14) and np.allclose(dK, 0, atol=1e-14)
+    assert np.allclose(dV[0, 0, 0], dO[0, 0].sum(axis=0), atol=1e-13)
+    # Q = 0: P is uniform over the visible keys, dV_j = sum over rows i that see j of dO_i / n_i
+    n_q, n_k = 5, 8
+    dO = rng.standard_normal((1, 1, n_q, 3))
+    K, V = rng.standard_normal((1, 1, n_k, 3)), rng.standard_normal((1, 1, n_k, 3))
+    _, _, dV = orc.attention_backward(np.zeros((1, 1, n_q, 3)), K, V, dO, 1.0, True)
+    want = np.zeros((n_k, 3))
+    for i in range(n_q):
+        seen = i + (n_k - n_q) + 1
+        for j in range(seen):
+            want[j] += dO[0, 0, i] / seen
+    assert np.allclose(dV[0, 0], want, atol=1e-14)
+    # adding one vector to every key leaves each softmax row unchanged: sum_j dK_j = 0
+    Q, dO = rng.standard_normal((2, 4, 9, 5)), rng.standard_normal((2, 4, 9, 5))
+    K, V = rng.standard_normal((2, 2, 12, 5)), rng.standard_normal((2, 2, 12, 5))
+    _, dK, _ = orc.attention_backward(Q, K, V, dO, 0.3, True)
+    assert np.allclose(dK.sum(axis=2), 0, atol=1e-12)
+    # rows that see no key (causal, N_q > N_k) get dQ = 0 and add nothing to dK, dV
+    Q, dO = rng.standard_normal((1, 2, 6, 4)), rng.standard_normal((1, 2, 6, 4))
+    K, V = rng.standard_normal((1, 1, 3, 4)), rng.standard_normal((1, 1, 3, 4))
+    dQ, dK, dV = orc.attention_backward(Q, K, V, dO, 0.6, True)
+    dQ2, dK2, dV2 = orc.attention_backward(Q[:, :, 3:], K, V, dO[:, :, 3:], 0.6, True)
+    assert np.allclose(dQ[:, :, :3], 0, atol=1e-15)
+    assert np.allclose(dQ[:, :, 3:], dQ2, atol=1e-14)
+    assert np.allclose(dK, dK2, atol=1e-14) and np.allclose(dV, dV2, atol=1e-14)
+
+
+def check_backward_saved_state(orc):
+    """The page's recipe: P rebuilt as exp(S - LSE) from the forward's LSE is the softmax,
+    and D = rowsum(dO * O) equals sum_j P_ij dP_ij; the gradients built from those saved
+    values equal the oracle's."""
+    rng = np.random.default_rng(24)
+    n_q, n_k, d, scale = 11, 17, 6, 0.45
+    q, k, v, do = (rng.standard_normal(s) for s in ((n_q, d), (n_k, d), (n_k, d), (n_q, d)))
+    O, lse = orc.attention_head(q, k, v, scale, True)
+    vis = np.array([[j <= i + (n_k - n_q) for j in range(n_k)] for i in range(n_q)])
+    S = np.where(vis, scale * (q @ k.T), -np.inf)
+    P = np.exp(S - lse[:, None])
+    assert np.allclose(P.sum(axis=1), 1.0, atol=1e-14)
+    D = np.sum(do * O, axis=1)
+    dP = do @ v.T
+    assert np.allclose(D, np.sum(P * dP, axis=1), atol=1e-12)
+    dS = P * (dP - D[:, None])
+    dq, dk, dv = orc.attention_head_backward(q, k, v, do, scale, True)
+    assert np.allclose(dq, scale * dS @ k, atol=1e-12)
+    assert np.allclose(dk, scale * dS.T @ q, atol=1e-12)
+    assert np.allclose(dv, P.T @ do, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_softmax_123, check_online_numbers, check_lse_merge_numbers, check_decode_mask,
     check_mask_counts_closed_form, check_v_identity_gives_probabilities, check_v_ones,
     check_vs_sdpa, check_gqa_is_mha_on_repeated_kv, check_paged_equals_contiguous,
     check_merge_partition_invariance, check_online_equals_two_pass,
+    check_backward_vs_autograd, check_backward_finite_differences, check_backward_closed_forms,
+    check_backward_saved_state,
 ]

@@ -13,6 +13,47 @@ real_visible_mask = orc.visible_mask
 real_gather_pages = orc.gather_pages
 real_lse_merge = orc.lse_merge
 real_online_fa2 = orc.online_softmax_fa2
+real_head_backward = orc.attention_head_backward
+
+
+def _head_backward_variant(kind):
+    """attention_head_backward with one planted mistake of the given kind."""
+    def mutant(q, k, v, do, scale, causal, row_chunk=512):
+        q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+        n_q, n_k = q.shape[0], k.shape[0]
+        x = scale * (q @ k.T)
+        x = np.where(orc.visible_mask(n_q, n_k, causal), x, -np.inf)
+        m = np.max(x, axis=1, keepdims=True)
+        e = np.exp(x - np.where(np.isfinite(m), m, 0.0))
+        l = np.sum(e, axis=1, keepdims=True)
+        p = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
+        o = p @ v
+        D = np.sum(do * o, axis=1)
+        dp = do @ v.T
+        ds = {"no_D": p * dp, "sign": p * (D[:, None] - dp)}.get(kind, p * (dp - D[:, None]))
+        dq = (ds @ k) if kind == "dq_no_scale" else scale * (ds @ k)
+        dk = scale * (ds.T @ (do if kind == "dk_wrong_operand" else q))
+        dv = (ds.T @ do) if kind == "dv_uses_ds" else p.T @ do
+        return dq, dk, dv
+    mutant.__doc__ = {"no_D": "backward: dS = P * dP (D dropped)",
+                      "sign": "backward: dS = P * (D - dP) (sign flipped)",
+                      "dq_no_scale": "backward: dQ without the scale",
+                      "dk_wrong_operand": "backward: dK = scale dS^T dO instead of dS^T Q",
+                      "dv_uses_ds": "backward: dV = dS^T dO instead of P^T dO"}[kind]
+    return mutant
+
+
+def backward_gqa_last_head(Q, K, V, dO, scale, causal, heads=None):
+    """backward GQA: dK/dV of a KV head taken from the last head of its group, not the sum"""
+    B, H_q = Q.shape[:2]
+    H_kv = K.shape[1]
+    g = H_q // H_kv
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    for b in range(B):
+        for h in range(H_q):
+            dq, dk, dv = real_head_backward(Q[b, h], K[b, h // g], V[b, h // g], dO[b, h], scale, causal)
+            dQ[b, h], dK[b, h // g], dV[b, h // g] = dq, dk, dv
+    return dQ, dK, dV
 
 
 def mask_strict(n_q, n_k, causal, rows=None):
@@ -113,6 +154,12 @@ MUTANTS = [
     ("gather_pages", gather_swapped),
     ("lse_merge", merge_unnormalized),
     ("online_softmax_fa2", online_no_rescale),
+    ("attention_head_backward", _head_backward_variant("no_D")),
+    ("attention_head_backward", _head_backward_variant("sign")),
+    ("attention_head_backward", _head_backward_variant("dq_no_scale")),
+    ("attention_head_backward", _head_backward_variant("dk_wrong_operand")),
+    ("attention_head_backward", _head_backward_variant("dv_uses_ds")),
+    ("attention_backward", backward_gqa_last_head),
 ]
 
 
