@@ -11,7 +11,8 @@ the stream the library launches on) against the dense bf16 MFMA peak (prefill) o
 HBM peak (decode), with ``traffic`` taken from the committed rocprofv3 counter summary
 when it was measured on the current kernel source.  ``breakdown`` adds the other
 prefill variants, the long causal prefill, the chunked prefill over a paged cache (FLOPs:
-4 d per visible query-key pair, exact) and the two decode workloads (decode timed with L2
+4 d per visible query-key pair, exact), the backward pass at the prefill shape (FLOPs: 2.5x
+the forward's) and the two decode workloads (decode timed with L2
 and the Infinity Cache flushed by a 1 GiB read before every call).  ``cpu_baseline`` times
 the fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
 
@@ -37,7 +38,8 @@ PREFILL = {
 }
 DECODE = ("decode_splitkv_128k", "decode_paged_b64")
 PAGED_PREFILL = ("chunked_prefill_paged",)
-WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + PAGED_PREFILL + DECODE
+BACKWARD = ("backward",)
+WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + PAGED_PREFILL + BACKWARD + DECODE
 
 
 def parse():
@@ -103,6 +105,8 @@ def main():
             return workloads.long_prefill_8192()
         if name == "chunked_prefill_paged":
             return workloads.chunked_prefill_paged()
+        if name == "backward":
+            return workloads.backward_4x16x4096()
         if name == "decode_splitkv_128k":
             return workloads.decode_splitkv_128k()
         return workloads.decode_paged_b64()
@@ -131,7 +135,27 @@ def main():
                             stream=stream)
         return fn, flops, (q, k, v, bt, o, lse)
 
+    def backward_case(wd):
+        """fa_bwd (D prep + dQ + dK/dV kernels) on the forward's own O and LSE; FLOPs are
+        2.5x the forward's (five products of 2 N_q N_k d each, halved for causal), the
+        usual count, although the dQ kernel recomputes two of them."""
+        w, do = wd
+        q, k, v, g = (t.to(dev) for t in (w.q, w.k, w.v, do))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fa.fa_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        s = w.shape
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(s["B"], s["H_q"], s["N_q"]), dtype=torch.uint8, device=dev)
+        flops = 2.5 * rl.prefill_flops(s["B"], s["H_q"], s["N_q"], s["N_k"], s["d"], w.causal)
+
+        def fn():
+            fa.fa_bwd(q, k, v, o, g, lse, dq, dk, dv, causal=w.causal, scale=w.scale, workspace=ws, stream=stream)
+        return fn, flops, (q, k, v, g, o, lse, dq, dk, dv, ws)
+
     def any_prefill_case(w):
+        if isinstance(w, tuple):
+            return backward_case(w)
         return paged_prefill_case(w) if w.name.startswith("chunked_prefill") else prefill_case(w)
 
     def decode_case(w, ns):
@@ -162,6 +186,9 @@ def main():
     # ---- the timed workload ----
     head = args.workload
     w = make(head)
+    w_inputs = w
+    if head in BACKWARD:
+        w = w[0]
     s = w.shape
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
     if head in DECODE:
@@ -178,7 +205,7 @@ def main():
             "paged": w.block_table is not None}
     else:
         paged = head in PAGED_PREFILL
-        fn, flops, bufs = any_prefill_case(w)
+        fn, flops, bufs = any_prefill_case(w_inputs)
         total_ms, per = timed(fn, args.steps, args.warmup)
         avg = statistics.mean(per)
         ms_per_step = total_ms / args.steps
@@ -186,6 +213,8 @@ def main():
         unit, bound, peak, achieved = "TFLOP/s", "mfma", rl.PEAK_BF16_MFMA_TFLOPS, flops / (avg * 1e-3) / 1e12
         kernel = (f"fa::fwd_bf16_kernel<{s['d']}, {64 if s['d'] == 128 else 128}, {str(w.causal).lower()}, "
                   f"{str(paged).lower()}, bf16>")
+        if head in BACKWARD:
+            kernel = "fa::bwd_prep_kernel + fa::bwd_dq_kernel + fa::bwd_dkdv_kernel (whole fa_bwd call)"
         extra_cfg = {"N_q": s["T"] if paged else s["N_q"], "N_k": s["N_k"], "causal": w.causal,
                      "flops_per_step": flops}
         if paged:
@@ -224,6 +253,8 @@ def main():
             fn, fl, bufs = any_prefill_case(ww)
             _, per = timed(fn, max(10, args.steps // 2), 3)
             med = statistics.median(per)
+            if isinstance(ww, tuple):
+                ww = ww[0]
             breakdown[ww.name] = {"us": round(med * 1e3, 2), "TFLOP/s": round(fl / med / 1e9, 2),
                                   "frac_mfma": round(fl / med / 1e9 / rl.PEAK_BF16_MFMA_TFLOPS, 4)}
             del bufs
@@ -261,7 +292,7 @@ def main():
         del a, b
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the timed workload ----
-    if not args.no_cpu and head not in DECODE:
+    if not args.no_cpu and head not in DECODE and head not in BACKWARD:
         result["cpu_baseline"] = cpu_baseline(w, rl)
 
     line = json.dumps(result)

@@ -14,6 +14,7 @@
  *   K, V            [B, H_kv, N_k, d]          (contiguous cache)
  *   K, V pools      [num_pages, page_size, H_kv, d]   (paged cache: fa_fwd_paged, decode)
  *   LSE             [B, H_q, N_q] fp32
+ *   dQ / dK, dV     as Q / as K, V   (fa_bwd)
  *   block_table     [B, pages_per_seq] int32
  *
  * Semantics (each output row is exact attention up to rounding):
@@ -100,6 +101,37 @@ int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LS
                  int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
                  const int32_t* block_table, int page_size, int pages_per_seq,
                  int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one 64-float record
+ * per 32 query rows of each (batch, query head) (the base-2 LSE and D of those rows),
+ * rounded up to 256 bytes.  Returns 0 on invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q);
+
+/*
+ * fa_bwd -- gradients of the forward pass: dQ, dK, dV for the upstream gradient dO.
+ *
+ * Defined by: page "Attention kernel chains", chain "What the backward pass saves": the
+ * forward keeps Q, K, V, O and one fp32 LSE per query row (fa_fwd's LSE output), each
+ * probability tile is rebuilt on chip as P = exp(S - LSE), and one extra row vector
+ * D = rowsum(dO * O) is computed before the main loops.  The rest is the chain rule of
+ * the forward definition: dP = dO V^T, dS = P * (dP - D), dV = P^T dO, dK = scale dS^T Q,
+ * dQ = scale dS K.  GQA: dK and dV of a KV head are summed over its H_q/H_kv query heads.
+ * The same bottom-right causal rule as fa_fwd.
+ *
+ *   Q, dO, O [B,H_q,N_q,d] bf16; K, V [B,H_kv,N_k,d] bf16; LSE [B,H_q,N_q] fp32 (from fa_fwd
+ *   on the same inputs, natural log; -inf for a row that sees no key).
+ *   dQ [B,H_q,N_q,d], dK and dV [B,H_kv,N_k,d]: bf16 (FA_BF16) or fp32 (FA_BF16_IN_FP32_OUT);
+ *   every element is written (keys no query sees get 0).
+ *   workspace: >= fa_bwd_workspace_bytes(B, H_q, N_q) bytes of device memory, 16-byte aligned.
+ *   d in {64, 128}.  scale > 0.  causal: 0 or 1.  stream: hipStream_t or NULL.
+ *   The result does not depend on scheduling (no atomics): repeated calls agree bit for bit.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV,
+           int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+           void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
  * fa_decode_num_splits -- the split count fa_decode_splitkv uses when called with

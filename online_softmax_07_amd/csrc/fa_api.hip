@@ -59,7 +59,7 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 101; }
+int fa_version(void) { return 102; }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
            int N_q, int N_k, int d, float scale, int causal, int dtype, void* stream) {
@@ -92,6 +92,28 @@ int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LS
     return FA_ERR_ALIGNMENT;
   fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
   return status_of(fa::launch_fwd_bf16_paged(a, dtype == FA_BF16_IN_FP32_OUT, block_table, page_size, pages_per_seq));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q) {
+  if (B < 1 || H_q < 1 || N_q < 1 || (long long)B * H_q * N_q > 0x7fffffffLL) return 0;
+  return fa::bwd_workspace_bytes(B, H_q, N_q);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
+           void* dK, void* dV, int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+           void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL_PTR;
+  int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
+  if (st != FA_OK) return st;
+  if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H_q, N_q)) return FA_ERR_WORKSPACE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned4(LSE) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+    return FA_ERR_ALIGNMENT;
+  fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H_q, H_kv, N_q, N_k, d, scale, causal, workspace, stream};
+  return status_of(fa::launch_bwd(a, dtype == FA_BF16_IN_FP32_OUT));
 }
 
 int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d) {

@@ -1,0 +1,548 @@
+// FlashAttention backward, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
+//
+// What is kept from the forward pass and how P comes back (page "Attention kernel chains",
+// chain "What the backward pass saves"): Q, K, V, O and one fp32 log-sum-exp per query row;
+// each probability tile is rebuilt on chip as P = exp(S - LSE), and the softmax gradient
+// uses one extra row vector D = rowsum(dO * O), computed once before the main loops.  With
+// dS = P * (dP - D), dP = dO V^T, the gradients are dV = P^T dO, dK = scale dS^T Q and
+// dQ = scale dS K (the chain rule of the forward definition).
+//
+// Three kernels on the caller's stream:
+//   * bwd_prep_kernel: per query row, D = rowsum(dO * O) and LSE in base 2, written to the
+//     workspace as one 64-float record per 32-row block (32 log2-LSE values, then 32 D
+//     values).  Rows past N_q, and rows that see no key, get LSE = +inf, so every P that
+//     refers to them is exactly 0 without a test.
+//   * bwd_dq_kernel: the forward's layout.  4 waves x 32 query rows own a 128-row block;
+//     K and V tiles of 64 keys stream through a double-buffered LDS ring (LDS-DMA loads).
+//     S^T = K Q^T and dP^T = V dO^T on the 32x32x16 MFMA put one query row in each lane,
+//     so LSE and D are per-lane scalars; dQ^T += K^T dS^T reads K^T with the transposing
+//     LDS read.  dQ is written once.
+//   * bwd_dkdv_kernel: the transposed roles.  4 waves x 32 keys own a 128-key block and
+//     hold their K and V rows as MFMA operands in registers; Q and dO tiles of 32 rows
+//     (of every query head of the GQA group in turn) stream through LDS.  S = Q K^T and
+//     dP = dO V^T put one key in each lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T
+//     and Q^T with the transposing LDS read.  dK and dV (summed over the group) are
+//     written once: no atomics, and the result does not depend on scheduling.
+// Both main kernels walk only the tiles the bottom-right causal mask leaves visible, and a
+// causal workgroup takes a heavy and a light block of one head so all cost the same.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kRowBlk = 32;    // rows per LSE/D record
+constexpr float kPosInf = __builtin_inff();
+
+// Logical 16-byte chunk c of LDS row r sits at position c ^ swz(r); keeps the plain b128
+// operand reads (16 rows, one chunk) and the transposing reads (4 rows x 4 chunks)
+// conflict-free on unpadded rows.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Workgroup -> (head, unit).  Workgroups are dispatched round-robin over the 8 XCDs; each
+// XCD gets a contiguous range of heads, so the blocks of one head share that XCD's L2.
+__device__ __forceinline__ void map_workgroup(int wg, int total_wg, int n_units, int& head, int& unit) {
+  const int n_heads = total_wg / n_units;
+  if ((n_heads & 7) == 0) {
+    const int hpx = n_heads >> 3;
+    const int x = wg & 7, idx = wg >> 3;
+    head = x * hpx + idx / n_units;
+    unit = idx % n_units;
+  } else {
+    int logical = wg;
+    if ((total_wg & 7) == 0) logical = (wg & 7) * (total_wg >> 3) + (wg >> 3);
+    head = logical / n_units;
+    unit = logical % n_units;
+  }
+}
+
+// Offsets (elements) of this lane's MFMA operand reads in a row-major swizzled LDS tile:
+//   plain: A/B fragment of k-step t (16 columns), row l32, logical chunk 2t + hh;
+//   transposing: column block cb, half r of a 16-row step: lane (g16, i16) points at row
+//     8r + 4hh + i16/4, columns 32cb + 16(g16%2) + 4(i16%4) .. +3.
+template <int D>
+struct OperandOffsets {
+  int plain[D / 16];
+  int tr[2][D / 32];
+  __device__ __forceinline__ OperandOffsets(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) plain[t] = l32 * D + 8 * ((2 * t + hh) ^ swz<D>(l32));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const int row = 8 * r + 4 * hh + (i16 >> 2);
+        const int c = 4 * cb + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        tr[r][cb] = row * D + 8 * (c ^ swz<D>(row)) + 4 * (i16 & 1);
+      }
+  }
+};
+
+// Transposed operand of a 16-row step starting at `row0` of an LDS tile: rows become k.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile, int row0, const OperandOffsets<D>& off, int cb) {
+  const __bf16* p = tile + row0 * D;
+  return join_bf16x8(lds_read_tr16(p + off.tr[0][cb]), lds_read_tr16(p + off.tr[1][cb]));
+}
+
+// Row-major store of a 32 x D accumulator block set (acc[cb] holds columns 32cb..32cb+31
+// of this lane's row, the MFMA layout of an O^T-style product), times `mul`.
+template <int D, typename OutT>
+__device__ __forceinline__ void store_row(OutT* row, const f32x16 (&acc)[D / 32], float mul, int hh) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = cb * 32 + 8 * g + 4 * hh;
+      const f32x4 v = {acc[cb][4 * g] * mul, acc[cb][4 * g + 1] * mul, acc[cb][4 * g + 2] * mul,
+                       acc[cb][4 * g + 3] * mul};
+      if constexpr (sizeof(OutT) == 4) {
+        *reinterpret_cast<f32x4*>(row + c) = v;
+      } else {
+        *reinterpret_cast<bf16x4*>(row + c) = __builtin_convertvector(v, bf16x4);
+      }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// D = rowsum(dO * O) and the base-2 LSE, per 32-row record
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const __bf16* __restrict__ O,
+                                                            const __bf16* __restrict__ dO,
+                                                            const float* __restrict__ LSE, float* __restrict__ rec,
+                                                            int N_q, int n_rblk, long long n_slots) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 values each
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long slot = t / LPR;  // one slot per padded row
+  const int part = (int)(t % LPR);
+  float acc = 0.f;
+  const long long bh = slot / ((long long)n_rblk * kRowBlk);
+  const int row = (int)(slot - bh * n_rblk * kRowBlk);
+  const bool valid = slot < n_slots && row < N_q;
+  if (valid) {
+    const size_t off = ((size_t)bh * N_q + row) * D + 8 * part;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + off);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)o[i], (float)g[i], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += shfl_xor_f(acc, m);
+  if (part == 0 && slot < n_slots) {
+    float l2 = kPosInf;  // rows past N_q and rows with no visible key: every P is 0
+    if (valid) {
+      const float l = LSE[(size_t)bh * N_q + row];
+      if (l != kNegInf) l2 = l * kLog2e;
+    }
+    const long long blk = bh * n_rblk + row / kRowBlk;
+    rec[blk * 64 + (row % kRowBlk)] = l2;
+    rec[blk * 64 + 32 + (row % kRowBlk)] = valid ? acc : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ: one workgroup per 128 query rows (causal: a heavy and a light block), K/V streamed
+// ---------------------------------------------------------------------------------------
+template <int D, bool CAUSAL, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ rec, OutT* __restrict__ dQ, int H_q, int H_kv,
+    int N_q, int N_k, float scale, float scale_log2, int n_qblocks, int n_units, int total_wg) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int CHUNKS = D / 8;
+  constexpr int STAGE = BC * D;
+  constexpr int ROWS_PER_DMA = 1024 / (2 * D);
+  constexpr int DMA = BC * D * 2 / 1024 / 4;  // per wave per tile, K and V each
+  constexpr int NCB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks0[STAGE], Ks1[STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs0[STAGE], Vs1[STAGE];
+
+  int bh, unit;
+  map_workgroup(blockIdx.x, total_wg, n_units, bh, unit);
+  const int b = bh / H_q;
+  const int h = bh - b * H_q;
+  const int hk = h / (H_q / H_kv);
+  const __bf16* Kp = K + ((size_t)b * H_kv + hk) * N_k * D;
+  const __bf16* Vp = V + ((size_t)b * H_kv + hk) * N_k * D;
+  const int n_rblk = (N_q + kRowBlk - 1) / kRowBlk;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const OperandOffsets<D> off(lane);
+  uint32_t dma_off[DMA];
+#pragma unroll
+  for (int i = 0; i < DMA; ++i) {
+    const int r = ROWS_PER_DMA * (DMA * wave + i) + lane / CHUNKS;
+    dma_off[i] = (uint32_t)(r * D + 8 * ((lane % CHUNKS) ^ swz<D>(r))) * 2u;
+  }
+  auto tile_rsrc = [&](const __bf16* base, int j) {
+    const int kbase = j * BC;
+    return make_rsrc(base + (size_t)kbase * D, range_bytes((long long)N_k - kbase, D * 2));
+  };
+
+  const int n_pass = (CAUSAL && 2 * unit + 1 < n_qblocks) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int qb = !CAUSAL ? unit : (pass == 0 ? n_qblocks - 1 - unit : unit);
+    const int q0 = qb * BR;
+    const int wave_row0 = q0 + wave * 32;
+    const int qrow = wave_row0 + l32;
+    const int shift = N_k - N_q;
+    const int qr = qrow < N_q ? qrow : N_q - 1;
+
+    bf16x8 qf[D / 16], gf[D / 16];  // Q and dO rows as MFMA B fragments
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = *reinterpret_cast<const bf16x8*>(Q + ((size_t)bh * N_q + qr) * D + 16 * t + 8 * hh);
+      gf[t] = *reinterpret_cast<const bf16x8*>(dO + ((size_t)bh * N_q + qr) * D + 16 * t + 8 * hh);
+      if (qrow >= N_q) gf[t] = bf16x8{};
+    }
+    const float* r = rec + ((size_t)bh * n_rblk + qr / kRowBlk) * 64 + (qr % kRowBlk);
+    const float lse2 = qrow < N_q ? r[0] : kPosInf;
+    const float Dv = qrow < N_q ? r[32] : 0.f;
+
+    int n_tiles = (N_k + BC - 1) / BC;
+    if (CAUSAL) {
+      const int max_key = min(q0 + BR - 1, N_q - 1) + shift;
+      n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
+    }
+    const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;
+    const int row_lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1;
+
+    f32x16 dq[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
+
+    auto dma = [&](int i, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, __bf16* ks, __bf16* vs) {
+      const int ii = i % DMA;
+      buffer_load16_lds(i < DMA ? kr : vr, dma_off[ii], (i < DMA ? ks : vs) + (DMA * wave_u + ii) * 512);
+    };
+    if (n_tiles > 0) {
+      const auto kr = tile_rsrc(Kp, 0), vr = tile_rsrc(Vp, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DMA; ++i) dma(i, kr, vr, Ks0, Vs0);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    auto tile_step = [&](int j, const __bf16* ks, const __bf16* vs, __bf16* ks_next, __bf16* vs_next) {
+      const auto kr_next = tile_rsrc(Kp, j + 1), vr_next = tile_rsrc(Vp, j + 1);
+      constexpr int NDMA = 2 * DMA;
+      constexpr int STEPS = 2 * (D / 16);
+      constexpr int DMA_PER_STEP = (NDMA + STEPS - 1) / STEPS;
+      const int kbase = j * BC;
+      if (!CAUSAL || kbase <= wave_last_key) {
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) {
+          const int kb0 = kbase + kb * 32;
+          if (CAUSAL && kb0 > wave_last_key) {
+#pragma unroll
+            for (int i = kb * (D / 16) * DMA_PER_STEP; i < (kb + 1) * (D / 16) * DMA_PER_STEP && i < NDMA; ++i)
+              dma(i, kr_next, vr_next, ks_next, vs_next);
+            continue;
+          }
+          // S^T and dP^T of 32 keys x this wave's 32 rows
+          __builtin_amdgcn_s_setprio(1);
+          f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + off.plain[t]);
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + kb * 32 * D + off.plain[t]);
+            s = mfma32x32x16(ka, qf[t], s);
+            dp = mfma32x32x16(va, gf[t], dp);
+            const int st = kb * (D / 16) + t;
+#pragma unroll
+            for (int i = st * DMA_PER_STEP; i < (st + 1) * DMA_PER_STEP && i < NDMA; ++i)
+              dma(i, kr_next, vr_next, ks_next, vs_next);
+          }
+          __builtin_amdgcn_s_setprio(0);
+          // P^T = 2^(s scale log2e - lse2), 0 past the mask; dS^T = P^T (dP^T - D)
+          const bool need_mask = (kb0 + 32 > N_k) || (CAUSAL && kb0 + 31 > wave_row0 + shift);
+          const int thr = row_lim - kb0 - 4 * hh;
+          f32x16 ds;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float p = exp2f_hw(__builtin_fmaf(s[i], scale_log2, -lse2));
+            if (need_mask && 8 * (i >> 2) + (i & 3) > thr) p = 0.f;
+            ds[i] = p * (dp[i] - Dv);
+          }
+          bf16x8 dsf[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            dsf[u] = to_bf16x8(f32x8{ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3], ds[8 * u + 4],
+                                     ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
+          // dQ^T += K^T dS^T (K^T through the transposing LDS read)
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              dq[cb] = mfma32x32x16(tr_frag<D>(ks, kb * 32 + 16 * u, off, cb), dsf[u], dq[cb]);
+          __builtin_amdgcn_s_setprio(0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) dma(i, kr_next, vr_next, ks_next, vs_next);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+      tile_step(j, Ks0, Vs0, Ks1, Vs1);
+      if (j + 1 < n_tiles) tile_step(j + 1, Ks1, Vs1, Ks0, Vs0);
+    }
+    if (qrow < N_q) store_row<D>(dQ + ((size_t)bh * N_q + qrow) * D, dq, scale, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV: one workgroup per 128 keys of a KV head (causal: a heavy and a light block);
+// Q and dO of every query head of the group streamed past
+// ---------------------------------------------------------------------------------------
+template <int D, bool CAUSAL, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ rec, OutT* __restrict__ dK, OutT* __restrict__ dV,
+    int H_q, int H_kv, int N_q, int N_k, float scale, float scale_log2, int n_kblocks, int n_units, int total_wg) {
+  constexpr int BKV = 128, BQ = 32;
+  constexpr int CHUNKS = D / 8;
+  constexpr int STAGE = BQ * D;
+  constexpr int ROWS_PER_DMA = 1024 / (2 * D);
+  constexpr int TDMA = BQ * D * 2 / 1024;  // 1 KB loads per tile (Q or dO)
+  constexpr int DMA = 2 * TDMA / 4;        // per wave per step, Q and dO together
+  constexpr int NCB = D / 32;
+  static_assert(DMA * 4 == 2 * TDMA, "the Q and dO tiles must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) __bf16 Qs0[STAGE], Qs1[STAGE];
+  __shared__ __attribute__((aligned(16))) __bf16 Gs0[STAGE], Gs1[STAGE];
+  __shared__ __attribute__((aligned(16))) float Rs0[64], Rs1[64];  // log2 LSE[32], D[32]
+
+  int bhk, unit;
+  map_workgroup(blockIdx.x, total_wg, n_units, bhk, unit);
+  const int b = bhk / H_kv;
+  const int hk = bhk - b * H_kv;
+  const int g = H_q / H_kv;
+  const int n_rblk = (N_q + kRowBlk - 1) / kRowBlk;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const OperandOffsets<D> off(lane);
+  // DMA i of this wave: global index gi = DMA*wave + i; the first TDMA fill Q, the rest dO
+  uint32_t dma_off[DMA];
+#pragma unroll
+  for (int i = 0; i < DMA; ++i) {
+    const int li = (DMA * wave + i) % TDMA;
+    const int r = ROWS_PER_DMA * li + lane / CHUNKS;
+    dma_off[i] = (uint32_t)(r * D + 8 * ((lane % CHUNKS) ^ swz<D>(r))) * 2u;
+  }
+  const int shift = N_k - N_q;
+  const int n_qb = (N_q + BQ - 1) / BQ;
+
+  const int n_pass = (CAUSAL && 2 * unit + 1 < n_kblocks) ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    // causal: early keys are seen by the most rows, so block `unit` is the heavy one
+    const int kblk = !CAUSAL ? unit : (pass == 0 ? unit : n_kblocks - 1 - unit);
+    const int k0 = kblk * BKV;
+    const int kw0 = k0 + 32 * wave;
+    const int key = kw0 + l32;
+    const int kr_ = key < N_k ? key : N_k - 1;
+
+    // this wave's K and V rows as MFMA B fragments (zero past N_k)
+    bf16x8 kf[D / 16], vf[D / 16];
+    const __bf16* Krow = K + (((size_t)b * H_kv + hk) * N_k + kr_) * D;
+    const __bf16* Vrow = V + (((size_t)b * H_kv + hk) * N_k + kr_) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      kf[t] = *reinterpret_cast<const bf16x8*>(Krow + 16 * t + 8 * hh);
+      vf[t] = *reinterpret_cast<const bf16x8*>(Vrow + 16 * t + 8 * hh);
+      if (key >= N_k) {
+        kf[t] = bf16x8{};
+        vf[t] = bf16x8{};
+      }
+    }
+    f32x16 dk[NCB], dv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      dk[cb] = f32x16{};
+      dv[cb] = f32x16{};
+    }
+
+    // query blocks that see a key of this workgroup: rows i >= k0 - shift (causal)
+    const int first_row = CAUSAL ? max(0, k0 - shift) : 0;
+    const int qb_first = first_row / BQ;
+    const int n_steps = first_row < N_q ? g * (n_qb - qb_first) : 0;
+    const int wave_first_row = CAUSAL ? kw0 - shift : -1;  // rows below see none of this wave's keys
+
+    auto step_rows = [&](int s, int& bh, int& q0) {
+      const int hi = s / (n_qb - qb_first);
+      bh = b * H_q + hk * g + hi;
+      q0 = (qb_first + (s - hi * (n_qb - qb_first))) * BQ;
+    };
+    auto issue = [&](int s, __bf16* qs, __bf16* gs, float* rs) {
+      int bh = 0, q0 = 0;
+      if (s < n_steps) step_rows(s, bh, q0);
+      const uint32_t bytes = s < n_steps ? range_bytes((long long)N_q - q0, D * 2) : 0u;
+      const auto qr = make_rsrc(Q + ((size_t)bh * N_q + q0) * D, bytes);
+      const auto gr = make_rsrc(dO + ((size_t)bh * N_q + q0) * D, bytes);
+#pragma unroll
+      for (int i = 0; i < DMA; ++i) {
+        const int gi = DMA * wave_u + i;  // wave-uniform
+        const int li = gi % TDMA;
+        buffer_load16_lds(gi < TDMA ? qr : gr, dma_off[i], (gi < TDMA ? qs : gs) + li * 512);
+      }
+      if (wave_u == 0 && lane < 16) {  // the 64-float LSE/D record of these 32 rows
+        const auto rr = make_rsrc(rec + ((size_t)bh * n_rblk + q0 / kRowBlk) * 64, s < n_steps ? 256u : 0u);
+        buffer_load16_lds(rr, (uint32_t)lane * 16u, reinterpret_cast<__bf16*>(rs));
+      }
+    };
+
+    issue(0, Qs0, Gs0, Rs0);
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](int s, const __bf16* qs, const __bf16* gs, const float* rs, __bf16* qs_n, __bf16* gs_n,
+                    float* rs_n) {
+      issue(s + 1, qs_n, gs_n, rs_n);
+      int bh, q0;
+      step_rows(s, bh, q0);
+      if (!CAUSAL || q0 + BQ - 1 >= wave_first_row) {
+        // S = Q K^T and dP = dO V^T for these 32 rows x this wave's 32 keys
+        __builtin_amdgcn_s_setprio(1);
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + off.plain[t]);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gs + off.plain[t]);
+          sc = mfma32x32x16(qa, kf[t], sc);
+          dp = mfma32x32x16(ga, vf[t], dp);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf),
+        // dS = P (dP - D[row]).  Register i holds row 8(i/4) + 4hh + i%4.
+        const bool need_mask = (kw0 + 32 > N_k) || (CAUSAL && kw0 + 31 > q0 + shift);
+        const int thr = q0 + 4 * hh + shift - key;  // key visible to row r iff r + thr >= 0
+        f32x16 p, ds;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rs + 8 * gq + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rs + 32 + 8 * gq + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            float pv = exp2f_hw(__builtin_fmaf(sc[i], scale_log2, -l4[e]));
+            if (need_mask && (key >= N_k || (CAUSAL && 8 * gq + e + thr < 0))) pv = 0.f;
+            p[i] = pv;
+            ds[i] = pv * (dp[i] - d4[e]);
+          }
+        }
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          pf[u] = to_bf16x8(f32x8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3], p[8 * u + 4], p[8 * u + 5],
+                                  p[8 * u + 6], p[8 * u + 7]});
+          dsf[u] = to_bf16x8(f32x8{ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3], ds[8 * u + 4],
+                                   ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            dv[cb] = mfma32x32x16(tr_frag<D>(gs, 16 * u, off, cb), pf[u], dv[cb]);
+            dk[cb] = mfma32x32x16(tr_frag<D>(qs, 16 * u, off, cb), dsf[u], dk[cb]);
+          }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int s = 0; s < n_steps; s += 2) {
+      step(s, Qs0, Gs0, Rs0, Qs1, Gs1, Rs1);
+      if (s + 1 < n_steps) step(s + 1, Qs1, Gs1, Rs1, Qs0, Gs0, Rs0);
+    }
+    if (key < N_k) {
+      const size_t row = (((size_t)b * H_kv + hk) * N_k + key) * D;
+      store_row<D>(dK + row, dk, scale, hh);
+      store_row<D>(dV + row, dv, 1.f, hh);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+namespace {
+
+template <int D, bool CAUSAL, typename OutT>
+hipError_t launch_bwd_main(const BwdArgs& a) {
+  hipStream_t st = (hipStream_t)a.stream;
+  const float scale_log2 = a.scale * kLog2e;
+  const float* rec = static_cast<const float*>(a.workspace);
+  {
+    const int n_qblocks = (a.N_q + 127) / 128;
+    const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;
+    const long long total = (long long)a.B * a.H_q * n_units;
+    if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, OutT>), dim3((unsigned)total), dim3(kThreads), 0, st,
+                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO, rec,
+                       (OutT*)a.dQ, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale, scale_log2, n_qblocks, n_units,
+                       (int)total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_kblocks = (a.N_k + 127) / 128;
+  const int n_units = CAUSAL ? (n_kblocks + 1) / 2 : n_kblocks;
+  const long long total = (long long)a.B * a.H_kv * n_units;
+  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OutT>), dim3((unsigned)total), dim3(kThreads), 0, st,
+                     (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO, rec,
+                     (OutT*)a.dK, (OutT*)a.dV, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale, scale_log2, n_kblocks,
+                     n_units, (int)total);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, bool out_f32) {
+  const int n_rblk = (a.N_q + kRowBlk - 1) / kRowBlk;
+  const long long n_slots = (long long)a.B * a.H_q * n_rblk * kRowBlk;
+  const long long threads = n_slots * (D / 8);
+  const long long grid = (threads + kThreads - 1) / kThreads;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)a.stream,
+                     (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, static_cast<float*>(a.workspace), a.N_q,
+                     n_rblk, n_slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.causal)
+    return out_f32 ? launch_bwd_main<D, true, float>(a) : launch_bwd_main<D, true, __bf16>(a);
+  return out_f32 ? launch_bwd_main<D, false, float>(a) : launch_bwd_main<D, false, __bf16>(a);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H_q, int N_q) {
+  const size_t n_rblk = ((size_t)N_q + kRowBlk - 1) / kRowBlk;
+  return ((size_t)B * H_q * n_rblk * 64 * sizeof(float) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, bool out_f32) {
+  return a.d == 128 ? launch_bwd_d<128>(a, out_f32) : launch_bwd_d<64>(a, out_f32);
+}
+
+}  // namespace fa

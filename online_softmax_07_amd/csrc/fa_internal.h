@@ -39,6 +39,23 @@ struct DecodeArgs {
   void* stream;
 };
 
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H_q, H_kv, N_q, N_k, d;
+  float scale;
+  int causal;
+  void* workspace;  // >= bwd_workspace_bytes(B, H_q, N_q)
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32);
 hipError_t launch_fwd_bf16_paged(const FwdArgs& a, bool out_f32, const int32_t* block_table, int page_size,
                                  int pages_per_seq);
@@ -46,6 +63,9 @@ hipError_t launch_fwd_fp32(const FwdArgs& a);
 hipError_t launch_decode_split(const DecodeArgs& a, bool out_f32);
 hipError_t launch_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE,
                             int num_splits, int rows, int d, bool out_f32, void* stream);
+
+size_t bwd_workspace_bytes(int B, int H_q, int N_q);
+hipError_t launch_bwd(const BwdArgs& a, bool out_f32);
 
 constexpr int kDecodeChunk = 64;  // keys per wave iteration in the decode kernel
 

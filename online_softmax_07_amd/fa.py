@@ -23,7 +23,7 @@ from . import build as _build
 FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_ALIGNMENT, FA_ERR_HIP = range(7)
 FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
 
-EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
             "fa_lse_merge", "fa_status_string", "fa_version")
 
 _lib = None
@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i
     L.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp]
     L.fa_fwd_paged.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, i, vp]
+    L.fa_bwd.restype = i
+    L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    L.fa_bwd_workspace_bytes.restype = sz
     L.fa_decode_num_splits.argtypes = [i, i, i, i, i, i]
     L.fa_decode_num_splits.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -199,6 +203,53 @@ def fa_fwd_paged(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_table:
                             int(pages_per_seq), dtype, _stream(stream, q.device))
     _raise(st, "fa_fwd_paged")
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def fa_bwd_workspace_bytes(B, H_q, N_q) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H_q, N_q))
+
+
+def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, do: torch.Tensor,
+           lse: torch.Tensor, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+           dv: Optional[torch.Tensor] = None, *, causal: bool = False, scale: Optional[float] = None,
+           out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """dQ, dK, dV of attention for the upstream gradient ``do``.  q, o, do [B,H_q,N_q,d] and
+    k, v [B,H_kv,N_k,d] bf16; lse [B,H_q,N_q] fp32 from fa_fwd on the same inputs.
+    Gradients are bf16 unless ``out_dtype=torch.float32`` (or fp32 ``dq``)."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    B, H_q, N_q, d = q.shape
+    _, H_kv, N_k, _ = k.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(t.dtype == torch.bfloat16, f"{name} must be bf16")
+    _need(k.shape == (B, H_kv, N_k, d) and v.shape == k.shape, "k/v shape mismatch")
+    _need(o.shape == q.shape and do.shape == q.shape, "o and do must have q's shape")
+    _need(lse.shape == (B, H_q, N_q) and lse.dtype == torch.float32, "lse must be fp32 [B,H_q,N_q]")
+    odt = out_dtype or (dq.dtype if dq is not None else torch.bfloat16)
+    _need(odt in (torch.bfloat16, torch.float32), "gradients must be bf16 or fp32")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=odt, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=odt, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=odt, device=q.device)
+    _need(dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape, "gradient shapes")
+    _need(dq.dtype == odt and dk.dtype == odt and dv.dtype == odt, "gradients must share one dtype")
+    need = fa_bwd_workspace_bytes(B, H_q, N_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check_dev(q.device, q=q, k=k, v=v, o=o, do=do, lse=lse, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H_q, H_kv, N_q, N_k, d, float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+                      FA_BF16 if odt == torch.bfloat16 else FA_BF16_IN_FP32_OUT, _stream(stream, q.device))
+    _raise(st, "fa_bwd")
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

@@ -18,6 +18,9 @@ The shapes are the pages' workloads:
   many splits for decode") and one GPU's share (H_q = 8, H_kv = 1) of a
   64-query-head / 8-KV-head model at batch 64, 8K context, 16-token pages
   ("GQA loads KV once per group", "The block-table cost of paged attention");
+* the attention backward at the prefill shape (B=4, H=16, N=4096, d=128, causal) with
+  an N(0,1) upstream gradient dO (Attention kernel chains, "What the backward pass
+  saves", sized there for N = 8192 and 32 heads);
 * chunked prefill over the same kind of paged cache: the last 2048 of 8192 positions
   of 4 sequences at 32 query / 8 KV heads (the decode model's head layout), 16-token
   pages ("The causal mask for a decode step": the new queries sit at the end).
@@ -135,6 +138,13 @@ def decode(B, H_q, H_kv, T, N_k, d, seed, causal=True, page_size=0, num_pages=No
                   page_size, list(num_splits))
 
 
+def grad_output(shape, seed) -> torch.Tensor:
+    """The upstream gradient dO for a backward step: iid N(0,1) rounded to bf16, from its
+    own seeded stream (so the forward inputs are the same with and without it)."""
+    rng = np.random.default_rng(seed)
+    return to_bf16(_normal(rng, shape))
+
+
 # The five workloads, by what they are.
 def single_head_fp32() -> Prefill:
     """Single head, non-causal, fp32, 128x64, scale 1/8."""
@@ -159,6 +169,14 @@ def decode_splitkv_128k() -> Decode:
     """B=1, T=1, H_q=32, H_kv=8, d=128, S=131072 contiguous, causal (bottom-right)."""
     return decode(1, 32, 8, 1, 131072, 128, seed=400, causal=True,
                   num_splits=(1, 8, 16, 32, 64), name="decode_splitkv_b1_hq32_hkv8_s131072")
+
+
+def backward_4x16x4096() -> tuple:
+    """The causal d=128 prefill inputs and a seeded dO of O's shape (seed 700): one
+    training step's attention backward at the prefill shape."""
+    w = prefill_4x16x4096(128, True)
+    w.name = "backward_b4_h16_n4096_d128_causal"
+    return w, grad_output(tuple(w.q.shape), 700)
 
 
 def chunked_prefill_paged() -> Decode:

@@ -274,7 +274,7 @@ def lse_merge(O_parts: np.ndarray, lse_parts: np.ndarray):
 # Backward pass
 # ---------------------------------------------------------------------------
 
-def attention_head_backward(q, k, v, do, scale: float, causal: bool, row_chunk: int = 512):
+def attention_head_backward(q, k, v, do, scale: float, causal: bool, o=None, row_chunk: int = 512):
     """Gradients dQ [n_q, d], dK [n_k, d], dV [n_k, d] of one head, in fp64, for the
     upstream gradient dO [n_q, d] of O = softmax(scale * q K^T, masked) V.
 
@@ -289,6 +289,10 @@ def attention_head_backward(q, k, v, do, scale: float, causal: bool, row_chunk: 
         dP  = dO V^T
         dS  = P * (dP - D)         (softmax Jacobian: dS_ij = P_ij (dP_ij - sum_t P_it dP_it))
         dQ  = scale dS K,          dK = scale dS^T q
+
+    ``o`` (optional): the output O [n_q, d] as the forward saved it (for instance rounded
+    to bf16); D is then taken from it, as the backward receives it.  Default: the exact O.
+    With the exact O the result is the exact gradient.
 
     Rows are taken ``row_chunk`` at a time only to bound memory; dK and dV are the
     sums of the chunks' contributions.
@@ -310,8 +314,8 @@ def attention_head_backward(q, k, v, do, scale: float, causal: bool, row_chunk: 
         e = np.exp(x - m_safe)
         l = np.sum(e, axis=1, keepdims=True)
         p = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
-        o = p @ v
-        D = np.sum(do[r] * o, axis=1)
+        o_rows = p @ v if o is None else np.asarray(o, dtype=np.float64)[r]
+        D = np.sum(do[r] * o_rows, axis=1)
         dv += p.T @ do[r]
         dp = do[r] @ v.T
         ds = p * (dp - D[:, None])
@@ -320,8 +324,9 @@ def attention_head_backward(q, k, v, do, scale: float, causal: bool, row_chunk: 
     return dq, dk, dv
 
 
-def attention_backward(Q, K, V, dO, scale: float, causal: bool, heads=None):
-    """dQ [B, H_q, N_q, d], dK and dV [B, H_kv, N_k, d] in fp64.
+def attention_backward(Q, K, V, dO, scale: float, causal: bool, heads=None, O=None):
+    """dQ [B, H_q, N_q, d], dK and dV [B, H_kv, N_k, d] in fp64.  ``O`` (optional): the
+    saved forward output [B, H_q, N_q, d] that D is taken from (default: the exact O).
 
     GQA (Attention kernel chains, "GQA loads KV once per group"): query head h reads
     KV head h // g, so the gradient of KV head hk is the sum over the g query heads
@@ -338,7 +343,8 @@ def attention_backward(Q, K, V, dO, scale: float, causal: bool, heads=None):
     todo = [(b, hk) for b in range(B) for hk in range(H_kv)] if heads is None else heads
     for b, hk in todo:
         for h in range(hk * g, (hk + 1) * g):
-            dq, dk, dv = attention_head_backward(Q[b, h], K[b, hk], V[b, hk], dO[b, h], scale, causal)
+            dq, dk, dv = attention_head_backward(Q[b, h], K[b, hk], V[b, hk], dO[b, h], scale, causal,
+                                                 o=None if O is None else O[b, h])
             dQ[b, h] = dq
             dK[b, hk] += dk
             dV[b, hk] += dv

@@ -411,6 +411,17 @@ def check_backward_saved_state(orc):
     assert np.allclose(dq, scale * dS @ k, atol=1e-12)
     assert np.allclose(dk, scale * dS.T @ q, atol=1e-12)
     assert np.allclose(dv, P.T @ do, atol=1e-12)
+    # D from a saved O that is off by dO_i * delta: dV is unchanged, D moves by
+    # delta_i |dO_i|^2, and dQ_i moves by -scale * delta_i |dO_i|^2 * (P K)_i
+    delta = rng.standard_normal(n_q) * 1e-3
+    o_saved = O + delta[:, None] * do
+    dq2, dk2, dv2 = orc.attention_head_backward(q, k, v, do, scale, True, o=o_saved)
+    dD = delta * np.sum(do * do, axis=1)
+    assert np.allclose(dv2, dv, atol=1e-14)
+    assert np.allclose(dq2 - dq, -scale * dD[:, None] * (P @ k), atol=1e-12)
+    assert np.allclose(dk2 - dk, -scale * (P * dD[:, None]).T @ q, atol=1e-12)
+    dq3, dk3, dv3 = orc.attention_head_backward(q, k, v, do, scale, True, o=O)
+    assert np.allclose(dq3, dq, atol=1e-13) and np.allclose(dk3, dk, atol=1e-13)
 
 
 ALL_CHECKS = [

@@ -48,7 +48,7 @@ def test_build_is_current():
 
 def test_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_version() == 101
+    assert L.fa_version() == 102
     for s in range(7):
         assert fa.fa_status_string(s).startswith(
             ["FA_OK", "FA_ERR_NULL_PTR", "FA_ERR_BAD_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
@@ -103,6 +103,37 @@ def fwd_paged(**kw):
 ])
 def test_fwd_paged_rejects(kw, status):
     assert fwd_paged(**kw) == status
+
+
+def bwd(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, dO=P, L=P, dQ=P, dK=P, dV=P, B=1, H_q=4, H_kv=2, N_q=100, N_k=90, d=128,
+             scale=0.1, causal=1, ws=P, wsb=1 << 20, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], a["dQ"], a["dK"], a["dV"], a["B"],
+                           a["H_q"], a["H_kv"], a["N_q"], a["N_k"], a["d"], a["scale"], a["causal"], a["ws"],
+                           a["wsb"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR), (dict(dO=None), fa.FA_ERR_NULL_PTR),
+    (dict(L=None), fa.FA_ERR_NULL_PTR), (dict(dK=None), fa.FA_ERR_NULL_PTR), (dict(dV=None), fa.FA_ERR_NULL_PTR),
+    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=-0.1), fa.FA_ERR_BAD_SHAPE), (dict(causal=2), fa.FA_ERR_BAD_SHAPE),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE),
+    (dict(dO=P + 8), fa.FA_ERR_ALIGNMENT), (dict(dK=P + 2), fa.FA_ERR_ALIGNMENT), (dict(L=P + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(ws=P + 4), fa.FA_ERR_ALIGNMENT),
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    # one 64-float record per 32 rows of each (batch, query head), rounded to 256 bytes
+    assert fa.fa_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 128 * 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1) == 256
+    assert fa.fa_bwd_workspace_bytes(1, 3, 33) == 3 * 2 * 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1) == 0
 
 
 def dec(**kw):

@@ -18,7 +18,7 @@ real_head_backward = orc.attention_head_backward
 
 def _head_backward_variant(kind):
     """attention_head_backward with one planted mistake of the given kind."""
-    def mutant(q, k, v, do, scale, causal, row_chunk=512):
+    def mutant(q, k, v, do, scale, causal, o=None, row_chunk=512):
         q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
         n_q, n_k = q.shape[0], k.shape[0]
         x = scale * (q @ k.T)
@@ -27,7 +27,7 @@ def _head_backward_variant(kind):
         e = np.exp(x - np.where(np.isfinite(m), m, 0.0))
         l = np.sum(e, axis=1, keepdims=True)
         p = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
-        o = p @ v
+        o = p @ v if (o is None or kind == "ignores_saved_o") else np.asarray(o, dtype=np.float64)
         D = np.sum(do * o, axis=1)
         dp = do @ v.T
         ds = {"no_D": p * dp, "sign": p * (D[:, None] - dp)}.get(kind, p * (dp - D[:, None]))
@@ -39,11 +39,12 @@ def _head_backward_variant(kind):
                       "sign": "backward: dS = P * (D - dP) (sign flipped)",
                       "dq_no_scale": "backward: dQ without the scale",
                       "dk_wrong_operand": "backward: dK = scale dS^T dO instead of dS^T Q",
-                      "dv_uses_ds": "backward: dV = dS^T dO instead of P^T dO"}[kind]
+                      "dv_uses_ds": "backward: dV = dS^T dO instead of P^T dO",
+                      "ignores_saved_o": "backward: D from the recomputed O, not the saved O passed in"}[kind]
     return mutant
 
 
-def backward_gqa_last_head(Q, K, V, dO, scale, causal, heads=None):
+def backward_gqa_last_head(Q, K, V, dO, scale, causal, heads=None, O=None):
     """backward GQA: dK/dV of a KV head taken from the last head of its group, not the sum"""
     B, H_q = Q.shape[:2]
     H_kv = K.shape[1]
@@ -159,6 +160,7 @@ MUTANTS = [
     ("attention_head_backward", _head_backward_variant("dq_no_scale")),
     ("attention_head_backward", _head_backward_variant("dk_wrong_operand")),
     ("attention_head_backward", _head_backward_variant("dv_uses_ds")),
+    ("attention_head_backward", _head_backward_variant("ignores_saved_o")),
     ("attention_backward", backward_gqa_last_head),
 ]
 
