@@ -344,13 +344,14 @@ def cpu_baseline(w, rl):
 
 def load_traffic(workload_name, fabuild):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel sources (else None)."""
+    current sources of that kernel (else None)."""
     path = os.path.join(HERE, "profiles", f"traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != fabuild.source_hash():
+    kind = t.get("kernel_family")
+    if kind is None or t.get("kernel_hash") != fabuild.kernel_hash(kind):
         return None
     return t.get("traffic_bytes_per_launch")
 
