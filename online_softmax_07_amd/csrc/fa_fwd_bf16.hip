@@ -1,7 +1,7 @@
 // FlashAttention forward, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
 //
 // Loop order (page "Softmax and FlashAttention", "Concept", FlashAttention-2): one
-// workgroup owns a block of BR = 128 query rows of one (batch, head) and streams the K/V
+// workgroup owns a block of BR query rows of one (batch, head) and streams the K/V
 // tiles of BC keys past it; each BR x BC score tile lives only in registers and is folded
 // into the running output with the online-softmax carries of page "Kernel visualization:
 // Flash Attention 1" ("Derivation", "The tiled version"): running max m, running sum l,
@@ -9,7 +9,7 @@
 // chain "The online softmax on numbers"), and the per-row LSE written once.
 //
 // MI355X mapping:
-//   * 4 waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
+//   * 4 or 8 waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
 //     32x32x16 bf16 MFMA: K (from LDS) is the A operand, the wave's Q rows (registers,
 //     loaded once) the B operand.  In the accumulator layout each lane owns ONE query row
 //     (lane % 32) and 16 keys per 32-key block, so the row max is a register reduction
@@ -42,19 +42,21 @@
 
 namespace fa {
 
-constexpr int kBR = 128;      // query rows per workgroup
-constexpr int kThreads = 256; // 4 waves
+// NW waves of 32 query rows per workgroup: 4 (BR = 128, two workgroups per CU) for causal
+// prefill, whose blocks differ in cost and pair up; 8 (BR = 256, one workgroup per CU, each
+// K/V tile shared by twice the rows) otherwise.
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
 
-template <int D, int BC>
+template <int D, int BC, int NW>
 struct FwdTile {
+  static constexpr int BR = 32 * NW;        // query rows per workgroup
   static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
   static constexpr int STAGE = BC * D;      // elements of one K or V stage (no padding)
   static constexpr int ROWS_PER_DMA = 1024 / (2 * D);   // rows one wave-wide 16-byte DMA fills
-  static constexpr int DMA = BC * D * 2 / 1024 / (kThreads / 64);  // DMAs per wave per tile (K, V each)
+  static constexpr int DMA = BC * D * 2 / 1024 / NW;  // DMAs per wave per tile (K, V each)
   static constexpr int NKB = BC / 32;       // 32-key blocks per tile
   static constexpr int NCB = D / 32;        // 32-column blocks of O^T
-  static_assert(DMA * 1024 * (kThreads / 64) == BC * D * 2, "tile must split evenly over the waves");
+  static_assert(DMA * 1024 * NW == BC * D * 2, "tile must split evenly over the waves");
   // Logical 16-byte chunk c of row r sits at position c ^ swz(r) of the row.  Rows are not
   // padded (a DMA fills 1 KiB contiguously); the swizzle spreads both the plain K reads
   // (16 rows, one chunk) and the transposing V reads (4 rows x 4 chunks) over all banks.
@@ -63,13 +65,13 @@ struct FwdTile {
   }
 };
 
-template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+template <int D, int BC, int NW, bool CAUSAL, bool PAGED, typename OutT>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
     float scale_log2, int n_qblocks, int n_units, int total_wg,
     const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, float inv_page_size) {
-  using T = FwdTile<D, BC>;
+  using T = FwdTile<D, BC, NW>;
   // Two K and two V stages as separate arrays: with the stage known at compile time the
   // compiler can tell that a tile's LDS reads do not touch the stage being refilled, and
   // does not wait for the refill before reading.
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int n_pass = (CAUSAL && 2 * unit + 1 < n_qblocks) ? 2 : 1;
   for (int pass = 0; pass < n_pass; ++pass) {
     const int qb = !CAUSAL ? unit : (pass == 0 ? n_qblocks - 1 - unit : unit);
-    const int q0 = qb * kBR;
+    const int q0 = qb * T::BR;
     const int wave_row0 = q0 + wave * 32;
     const int qrow = wave_row0 + l32;
     const int shift = N_k - N_q;   // bottom-right alignment: row i sees keys j <= i + shift
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     // ---- which K/V tiles this block visits ----
     int n_tiles = (N_k + BC - 1) / BC;
     if (CAUSAL) {
-      const int max_key = min(q0 + kBR - 1, N_q - 1) + shift;
+      const int max_key = min(q0 + T::BR - 1, N_q - 1) + shift;
       n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
     }
     const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;  // causal reach of this wave
@@ -279,6 +281,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
             dma(i, j + 1, kr_next, vr_next, pg_next, ks_next, vs_next);
         }
+        // order: fragments of two k-steps in flight ahead of the MFMAs that use them
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::NKB, 0);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, T::NKB, 0);
+          if (t * DMA_PER_STEP < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, DMA_PER_STEP, 0);
+          if (t + 2 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, T::NKB, 0);
+        }
 
         __builtin_amdgcn_s_setprio(0);
         // ---- mask: ragged tail and the bottom-right causal edge ----
@@ -391,11 +401,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
 template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
 static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_size, int pages_per_seq) {
-  const int n_qblocks = (a.N_q + kBR - 1) / kBR;
+  constexpr int NW = (CAUSAL && !PAGED) ? 4 : 8;
+  constexpr int BR = FwdTile<D, BC, NW>::BR;
+  const int n_qblocks = (a.N_q + BR - 1) / BR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
   const long long total = (long long)a.B * a.H_q * n_units;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, CAUSAL, PAGED, OutT>), dim3((unsigned)total), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, CAUSAL, PAGED, OutT>), dim3((unsigned)total), dim3(64 * NW), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (OutT*)a.O, a.LSE, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e, n_qblocks,
                      n_units, (int)total, block_table, page_size, pages_per_seq,
