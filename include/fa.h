@@ -104,8 +104,8 @@ int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LS
 
 /*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: one 64-float record
- * per 32 query rows of each (batch, query head) (the base-2 LSE and D of those rows),
- * rounded up to 256 bytes.  Returns 0 on invalid sizes.
+ * per 32 query rows of each (batch, query head) (the base-2 LSE and D of those rows), the
+ * rows padded to a multiple of 64, rounded up to 256 bytes.  Returns 0 on invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q);
 

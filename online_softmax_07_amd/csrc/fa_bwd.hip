@@ -10,16 +10,17 @@
 // Three kernels on the caller's stream:
 //   * bwd_prep_kernel: per query row, D = rowsum(dO * O) and LSE in base 2, written to the
 //     workspace as one 64-float record per 32-row block (32 log2-LSE values, then 32 D
-//     values).  Rows past N_q, and rows that see no key, get LSE = +inf, so every P that
-//     refers to them is exactly 0 without a test.
+//     values), rows padded to a multiple of 64.  Rows past N_q, and rows that see no key,
+//     get LSE = +inf, so every P that refers to them is exactly 0 without a test.
 //   * bwd_dq_kernel: the forward's layout.  4 waves x 32 query rows own a 128-row block;
 //     K and V tiles of 64 keys stream through a double-buffered LDS ring (LDS-DMA loads).
 //     S^T = K Q^T and dP^T = V dO^T on the 32x32x16 MFMA put one query row in each lane,
 //     so LSE and D are per-lane scalars; dQ^T += K^T dS^T reads K^T with the transposing
 //     LDS read.  dQ is written once.
 //   * bwd_dkdv_kernel: the transposed roles.  4 waves x 32 keys own a 128-key block and
-//     hold their K and V rows as MFMA operands in registers; Q and dO tiles of 32 rows
-//     (of every query head of the GQA group in turn) stream through LDS.  S = Q K^T and
+//     hold their K and V rows as MFMA operands in registers; Q and dO tiles of 64 rows
+//     (of every query head of the GQA group in turn) stream through LDS and are taken in
+//     two 32-row halves.  S = Q K^T and
 //     dP = dO V^T put one key in each lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T
 //     and Q^T with the transposing LDS read.  dK and dV (summed over the group) are
 //     written once: no atomics, and the result does not depend on scheduling.
@@ -34,6 +35,13 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowBlk = 32;    // rows per LSE/D record
+constexpr int kRecPerStep = 2; // records per dK/dV step (64 query rows)
+
+// LSE/D records per (batch, query head): whole steps of kRecPerStep records, so a step's
+// records always exist (rows past N_q are padding with LSE = +inf, D = 0).
+__host__ __device__ __forceinline__ int rec_blocks(int n_q) {
+  return (n_q + kRowBlk * kRecPerStep - 1) / (kRowBlk * kRecPerStep) * kRecPerStep;
+}
 constexpr float kPosInf = __builtin_inff();
 
 // Logical 16-byte chunk c of LDS row r sits at position c ^ swz(r); keeps the plain b128
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const int hk = h / (H_q / H_kv);
   const __bf16* Kp = K + ((size_t)b * H_kv + hk) * N_k * D;
   const __bf16* Vp = V + ((size_t)b * H_kv + hk) * N_k * D;
-  const int n_rblk = (N_q + kRowBlk - 1) / kRowBlk;
+  const int n_rblk = rec_blocks(N_q);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ rec, OutT* __restrict__ dK, OutT* __restrict__ dV,
     int H_q, int H_kv, int N_q, int N_k, float scale, float scale_log2, int n_kblocks, int n_units, int total_wg) {
-  constexpr int BKV = 128, BQ = 32;
+  constexpr int BKV = 128, BQ = kRowBlk * kRecPerStep, NSB = kRecPerStep;  // NSB 32-row sub-blocks
   constexpr int CHUNKS = D / 8;
   constexpr int STAGE = BQ * D;
   constexpr int ROWS_PER_DMA = 1024 / (2 * D);
@@ -326,14 +334,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   static_assert(DMA * 4 == 2 * TDMA, "the Q and dO tiles must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) __bf16 Qs0[STAGE], Qs1[STAGE];
   __shared__ __attribute__((aligned(16))) __bf16 Gs0[STAGE], Gs1[STAGE];
-  __shared__ __attribute__((aligned(16))) float Rs0[64], Rs1[64];  // log2 LSE[32], D[32]
+  __shared__ __attribute__((aligned(16))) float Rs0[64 * NSB], Rs1[64 * NSB];  // per 32 rows: log2 LSE[32], D[32]
 
   int bhk, unit;
   map_workgroup(blockIdx.x, total_wg, n_units, bhk, unit);
   const int b = bhk / H_kv;
   const int hk = bhk - b * H_kv;
   const int g = H_q / H_kv;
-  const int n_rblk = (N_q + kRowBlk - 1) / kRowBlk;
+  const int n_rblk = rec_blocks(N_q);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -405,8 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int li = gi % TDMA;
         buffer_load16_lds(gi < TDMA ? qr : gr, dma_off[i], (gi < TDMA ? qs : gs) + li * 512);
       }
-      if (wave_u == 0 && lane < 16) {  // the 64-float LSE/D record of these 32 rows
-        const auto rr = make_rsrc(rec + ((size_t)bh * n_rblk + q0 / kRowBlk) * 64, s < n_steps ? 256u : 0u);
+      if (wave_u == 0 && lane < 16 * NSB) {  // the 64-float LSE/D records of these rows
+        const auto rr = make_rsrc(rec + ((size_t)bh * n_rblk + q0 / kRowBlk) * 64, s < n_steps ? 256u * NSB : 0u);
         buffer_load16_lds(rr, (uint32_t)lane * 16u, reinterpret_cast<__bf16*>(rs));
       }
     };
@@ -420,27 +428,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       issue(s + 1, qs_n, gs_n, rs_n);
       int bh, q0;
       step_rows(s, bh, q0);
-      if (!CAUSAL || q0 + BQ - 1 >= wave_first_row) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+      const int qs0 = q0 + 32 * sb;  // first row of this sub-block
+      const __bf16* qsb = qs + sb * 32 * D;
+      const __bf16* gsb = gs + sb * 32 * D;
+      const float* rsb = rs + sb * 64;
+      if (!CAUSAL || qs0 + 31 >= wave_first_row) {
         // S = Q K^T and dP = dO V^T for these 32 rows x this wave's 32 keys
         __builtin_amdgcn_s_setprio(1);
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + off.plain[t]);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gs + off.plain[t]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qsb + off.plain[t]);
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gsb + off.plain[t]);
           sc = mfma32x32x16(qa, kf[t], sc);
           dp = mfma32x32x16(ga, vf[t], dp);
         }
         __builtin_amdgcn_s_setprio(0);
         // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf),
         // dS = P (dP - D[row]).  Register i holds row 8(i/4) + 4hh + i%4.
-        const bool need_mask = (kw0 + 32 > N_k) || (CAUSAL && kw0 + 31 > q0 + shift);
-        const int thr = q0 + 4 * hh + shift - key;  // key visible to row r iff r + thr >= 0
+        const bool need_mask = (kw0 + 32 > N_k) || (CAUSAL && kw0 + 31 > qs0 + shift);
+        const int thr = qs0 + 4 * hh + shift - key;  // key visible to row r iff r + thr >= 0
         f32x16 p, ds;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rs + 8 * gq + 4 * hh);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rs + 32 + 8 * gq + 4 * hh);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rsb + 8 * gq + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rsb + 32 + 8 * gq + 4 * hh);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * gq + e;
@@ -464,10 +478,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            dv[cb] = mfma32x32x16(tr_frag<D>(gs, 16 * u, off, cb), pf[u], dv[cb]);
-            dk[cb] = mfma32x32x16(tr_frag<D>(qs, 16 * u, off, cb), dsf[u], dk[cb]);
+            dv[cb] = mfma32x32x16(tr_frag<D>(gsb, 16 * u, off, cb), pf[u], dv[cb]);
+            dk[cb] = mfma32x32x16(tr_frag<D>(qsb, 16 * u, off, cb), dsf[u], dk[cb]);
           }
         __builtin_amdgcn_s_setprio(0);
+      }
       }
       wait_vmem();
       __syncthreads();
@@ -519,7 +534,7 @@ hipError_t launch_bwd_main(const BwdArgs& a) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, bool out_f32) {
-  const int n_rblk = (a.N_q + kRowBlk - 1) / kRowBlk;
+  const int n_rblk = rec_blocks(a.N_q);
   const long long n_slots = (long long)a.B * a.H_q * n_rblk * kRowBlk;
   const long long threads = n_slots * (D / 8);
   const long long grid = (threads + kThreads - 1) / kThreads;
@@ -537,7 +552,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool out_f32) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H_q, int N_q) {
-  const size_t n_rblk = ((size_t)N_q + kRowBlk - 1) / kRowBlk;
+  const size_t n_rblk = (size_t)rec_blocks(N_q);
   return ((size_t)B * H_q * n_rblk * 64 * sizeof(float) + 255) & ~(size_t)255;
 }
 

@@ -129,10 +129,11 @@ def test_bwd_rejects(kw, status):
 
 
 def test_bwd_workspace_bytes():
-    # one 64-float record per 32 rows of each (batch, query head), rounded to 256 bytes
+    # one 64-float record per 32 rows of each (batch, query head), rows padded to 64
     assert fa.fa_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 128 * 256
-    assert fa.fa_bwd_workspace_bytes(1, 1, 1) == 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1) == 2 * 256
     assert fa.fa_bwd_workspace_bytes(1, 3, 33) == 3 * 2 * 256
+    assert fa.fa_bwd_workspace_bytes(2, 3, 65) == 2 * 3 * 4 * 256
     assert fa.fa_bwd_workspace_bytes(0, 1, 1) == 0
 
 
