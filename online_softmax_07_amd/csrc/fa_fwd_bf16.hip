@@ -9,7 +9,7 @@
 // chain "The online softmax on numbers"), and the per-row LSE written once.
 //
 // MI355X mapping:
-//   * 4 or 8 waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
+//   * 8 (or 4) waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
 //     32x32x16 bf16 MFMA: K (from LDS) is the A operand, the wave's Q rows (registers,
 //     loaded once) the B operand.  In the accumulator layout each lane owns ONE query row
 //     (lane % 32) and 16 keys per 32-key block, so the row max is a register reduction
@@ -20,10 +20,11 @@
 //     the transposing LDS read (ds_read_b64_tr_b16), so V is staged exactly like K.
 //   * K/V tiles: 16-byte buffer loads that write LDS directly (no register staging), one
 //     tile ahead into a double-buffered LDS ring, issued a few at a time between the
-//     score MFMAs; zero past the end of the sequence; one barrier per tile.  Rows are stored unpadded with a 16-byte-chunk XOR swizzle that
-//     keeps the MFMA operand reads (plain for K, transposing for V) bank-conflict free.
-//   * Independent accumulators are interleaved and operand fragments are read one step
-//     ahead of the MFMA that consumes them.
+//     score MFMAs; zero past the end of the sequence; one barrier per tile.  Rows are
+//     stored unpadded with a 16-byte-chunk XOR swizzle that keeps the MFMA operand reads
+//     (plain for K, transposing for V) bank-conflict free.
+//   * Independent accumulators are interleaved; K fragments are read two k-steps ahead of
+//     the score MFMAs that consume them, V fragments one step ahead.
 //   * The running max is only moved (and l, O rescaled) when a row's tile max exceeds it
 //     by more than 2^8 in the exponent; until then p <= 2^8.  O = acc / l and
 //     LSE = m + ln l are exact for any reference m, so this only skips work (the skip is
@@ -42,9 +43,9 @@
 
 namespace fa {
 
-// NW waves of 32 query rows per workgroup: 4 (BR = 128, two workgroups per CU) for causal
-// prefill, whose blocks differ in cost and pair up; 8 (BR = 256, one workgroup per CU, each
-// K/V tile shared by twice the rows) otherwise.
+// NW waves of 32 query rows per workgroup.  The launches mostly use NW = 8 (BR = 256, one
+// workgroup and two waves per SIMD on each CU): every K/V tile staged in LDS serves 256 rows,
+// and the LDS freed by the second workgroup holds 128-key tiles at d = 128.
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
 
 template <int D, int BC, int NW>
@@ -401,7 +402,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
 
 template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
 static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_size, int pages_per_seq) {
-  constexpr int NW = (CAUSAL && !PAGED) ? 4 : 8;
+  // 8 waves; 4 (two 128-row workgroups per CU) measured 1-5 % slower, except causal d = 64
+  constexpr int NW = (D == 64 && CAUSAL && !PAGED) ? 4 : 8;
   constexpr int BR = FwdTile<D, BC, NW>::BR;
   const int n_qblocks = (a.N_q + BR - 1) / BR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
@@ -417,9 +419,12 @@ static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_
 
 template <int D, int BC, bool PAGED>
 static hipError_t dispatch_out(const FwdArgs& a, bool out_f32, const int32_t* bt, int ps, int pps) {
+  // d = 128: 128-key tiles (half the barriers per key) for contiguous K/V; the paged variant
+  // keeps 64-key tiles, whose per-lane page addressing would not fit the registers otherwise
+  constexpr int BC2 = (D == 128 && !PAGED) ? 128 : BC;
   if (a.causal)
-    return out_f32 ? launch<D, BC, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC, true, PAGED, __bf16>(a, bt, ps, pps);
-  return out_f32 ? launch<D, BC, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC, false, PAGED, __bf16>(a, bt, ps, pps);
+    return out_f32 ? launch<D, BC2, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC2, true, PAGED, __bf16>(a, bt, ps, pps);
+  return out_f32 ? launch<D, BC2, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC2, false, PAGED, __bf16>(a, bt, ps, pps);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32) {

@@ -5,9 +5,11 @@ Small cases compare every element: chunks that sit at the end of a longer cache 
 bottom-right mask), N_q = N_k, N_q > N_k (rows that see no key), GQA, page sizes that
 do not divide the key tile or the sequence, a page size of one and pages larger than a
 tile.  The full-size chunk compares sampled rows of every query block with the oracle.
-Both also check a property the oracle does not need: the paged result is bit-identical
-to fa_fwd on the same keys gathered into a contiguous cache, since both run the same
-arithmetic in the same order."""
+Both also compare with fa_fwd on the same keys gathered into a contiguous cache: at d = 64
+the two launches tile the keys alike and run the same arithmetic in the same order, so
+the results are bit-identical; at d = 128 the contiguous kernel takes 128-key tiles and
+the paged one 64-key tiles, so the two agree only to rounding (both are checked against
+the oracle above)."""
 
 import numpy as np
 import pytest
@@ -58,6 +60,22 @@ def same_bits(a, b, what):
                        b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)), what
 
 
+def agrees_with_contiguous(o, lse, oc, lc, d, what):
+    """Bit-identical at d = 64 (same tiling); at d = 128, equal to rounding: bf16 O within two
+    bf16 ulps of the larger value plus 1e-3, LSE within 1e-4."""
+    if d == 64:
+        same_bits(o, oc, what + ": O")
+        same_bits(lse, lc, what + ": LSE")
+        return
+    a, b = o.float(), oc.float()
+    tol = 2.0 ** -6 * torch.maximum(a.abs(), b.abs()) + 1e-3
+    assert bool(((a - b).abs() <= tol).all()), what + ": O"
+    fin = torch.isfinite(lc)
+    assert torch.equal(torch.isfinite(lse), fin), what + ": LSE -inf pattern"
+    if bool(fin.any()):
+        assert float((lse[fin] - lc[fin]).abs().max()) <= 1e-4, what + ": LSE"
+
+
 # B, H_q, H_kv, N_q, N_k, d, causal, page_size
 SMALL = [
     (1, 2, 1, 128, 300, 128, True, 16),      # a chunk at the end of the cache
@@ -89,8 +107,7 @@ def test_paged_prefill_small(case):
     check_lse(lse32, L)
     kc, vc = gathered(k, btd, Nk), gathered(v, btd, Nk)
     oc, lc = run_contiguous(q, kc, vc, causal, w.scale)
-    same_bits(o, oc, "O differs from fa_fwd on the gathered cache")
-    same_bits(lse, lc, "LSE differs from fa_fwd on the gathered cache")
+    agrees_with_contiguous(o, lse, oc, lc, d, "paged vs fa_fwd on the gathered cache")
 
 
 def test_paged_prefill_lse_optional():
@@ -105,8 +122,8 @@ def test_paged_prefill_lse_optional():
 
 def test_chunked_prefill_full_size():
     """The bench workload: 2048-token chunks over 8192 positions, 32/8 heads, 16-token
-    pages; every query block sampled, plus the bit-identity with the contiguous kernel
-    on every row."""
+    pages; every query block sampled, plus agreement with the contiguous kernel on every
+    row."""
     w = workloads.chunked_prefill_paged()
     s = w.shape
     say(w.name)
@@ -124,5 +141,4 @@ def test_chunked_prefill_full_size():
     kc, vc = gathered(k, bt, w.n_k), gathered(v, bt, w.n_k)
     del k, v
     oc, lc = run_contiguous(q, kc, vc, w.causal, w.scale)
-    same_bits(o, oc, "O differs from fa_fwd on the gathered cache")
-    same_bits(lse, lc, "LSE differs from fa_fwd on the gathered cache")
+    agrees_with_contiguous(o, lse, oc, lc, s["d"], "paged vs fa_fwd on the gathered cache")
