@@ -98,6 +98,8 @@ SMALL = [
     (1, 1, 1, 300, 33, 128, True),
     (1, 2, 1, 513, 513, 64, True),
     (2, 2, 2, 200, 1000, 128, False),
+    (1, 8, 1, 200, 300, 64, True),     # GQA group of 8, d = 64, chunk at the end
+    (1, 4, 2, 64, 64, 128, True),      # one 64-row step, one key block
 ]
 
 

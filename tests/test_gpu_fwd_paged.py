@@ -87,6 +87,8 @@ SMALL = [
     (3, 4, 1, 129, 4100, 128, True, 32),     # many tiles, GQA group of 4
     (1, 2, 1, 64, 700, 64, True, 256),       # pages larger than a tile
     (1, 2, 1, 257, 257, 64, False, 3),
+    (2, 8, 1, 150, 900, 64, True, 16),       # GQA group of 8 at d = 64
+    (1, 4, 4, 300, 2000, 128, False, 48),
 ]
 
 

@@ -1,0 +1,72 @@
+"""Host-side logic without a GPU: the FLOP and byte accounting the bench reports, the seeded
+input recipe, and the bench's refusal of a multi-GPU run."""
+
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from online_softmax_07_amd import roofline as rl, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def brute_pairs(n_q, n_k, causal):
+    return sum(sum(1 for j in range(n_k) if (not causal) or j <= i + n_k - n_q) for i in range(n_q))
+
+
+@pytest.mark.parametrize("n_q,n_k", [(1, 1), (1, 9), (9, 1), (5, 5), (7, 20), (20, 7), (64, 130), (33, 33)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_visible_pairs_brute_force(n_q, n_k, causal):
+    assert rl.visible_pairs(n_q, n_k, causal) == brute_pairs(n_q, n_k, causal)
+
+
+def test_flop_conventions():
+    # the prefill metric halves causal work; exact pair counting is one N(N+1)/2 * 4d per head
+    assert rl.prefill_flops(4, 16, 4096, 4096, 128, True) == 4.0 * 4096 * 4096 * 128 * 64 / 2
+    assert rl.chunked_prefill_flops(1, 1, 3, 3, 8, True) == 4 * 8 * 6
+    assert rl.chunked_prefill_flops(1, 1, 2, 5, 8, True) == 4 * 8 * (4 + 5)
+    # decode bytes: K and V once per KV head, plus Q, O, LSE and the table
+    assert rl.decode_bytes(1, 32, 8, 1, 131072, 128) == 536887424
+    assert rl.decode_bytes(64, 8, 1, 1, 8192, 128, pages_per_seq=512) == 268830720
+    assert rl.prefill_bytes_floor(4, 16, 16, 4096, 4096, 128) == 269484032
+
+
+def test_inputs_are_seeded_and_bf16_exact():
+    a = workloads.prefill(1, 2, 1, 33, 47, 64, seed=11, causal=True)
+    b = workloads.prefill(1, 2, 1, 33, 47, 64, seed=11, causal=True)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)):
+        assert x.dtype == torch.bfloat16 and torch.equal(x, y)
+    c = workloads.prefill(1, 2, 1, 33, 47, 64, seed=12, causal=True)
+    assert not torch.equal(a.q, c.q)
+    g1 = workloads.grad_output((1, 2, 33, 64), 5)
+    assert torch.equal(g1, workloads.grad_output((1, 2, 33, 64), 5))
+
+
+def test_paged_table_is_a_partial_permutation():
+    w = workloads.decode(3, 4, 2, 2, 100, 64, seed=9, page_size=16, num_pages=40)
+    bt = w.block_table.numpy()
+    assert bt.shape == (3, 7) and bt.dtype == np.int32
+    assert len(set(bt.ravel().tolist())) == bt.size          # no page used twice
+    assert bt.min() >= 0 and bt.max() < 40                   # every entry inside the pool
+    assert tuple(w.k.shape) == (40, 16, 2, 64)
+
+
+def test_heavy_rows_are_exact_multiples():
+    w = workloads.prefill(1, 1, 1, 16, 200, 64, seed=3, heavy_frac=0.01, causal=True)
+    rows = w.heavy_rows[0, 0]
+    assert len(rows) == 2 and len(set(rows.tolist())) == 2
+    plain = workloads.prefill(1, 1, 1, 16, 200, 64, seed=3, causal=True)
+    assert torch.equal(w.k[0, 0, rows].float(), 8 * plain.k[0, 0, rows].float())
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "single-GPU" in line["error"] and line["n_gpus"] == 2
