@@ -28,7 +28,12 @@
  *           (page "Kernel visualization: Flash Attention 1", "Derivation")
  *   LSE[b,h,i] = ln sum_j e^{x_j}  over visible j  (natural log of the scaled scores; chain
  *           "What the backward pass saves": one fp32 log-sum-exp per query row)
- *   A row with no visible key (causal with N_q > N_k) gets O = 0 and LSE = -inf.
+ *   A row with no visible key (causal with N_q > N_k, or N_k = 0) gets O = 0 and LSE = -inf.
+ *
+ * Sizes: B, H_q, H_kv and d are >= 1; the sequence lengths (N_q, N_k, T, rows) may be 0.
+ * A forward, decode or merge call with no query row validates its arguments and returns
+ * FA_OK without enqueuing anything.  A pointer to a tensor of zero elements may be NULL;
+ * any other may not.
  *
  * Errors: arguments are validated before anything is enqueued; on any failure nothing is
  * enqueued and a non-zero fa_status is returned.  A failed launch returns FA_ERR_HIP.
@@ -72,7 +77,7 @@ typedef enum fa_dtype {
  *   Q [B,H_q,N_q,d], K/V [B,H_kv,N_k,d] in `dtype`'s input type; O [B,H_q,N_q,d] in its
  *   output type; LSE [B,H_q,N_q] fp32 (may be NULL if not wanted).
  *   d in {64, 128}.  scale > 0 (typically 1/sqrt(d)).  causal: 0 or 1 (bottom-right).
- *   N_q, N_k >= 1, any value (ragged tails are masked).  stream: a hipStream_t or NULL.
+ *   N_q, N_k >= 0, any value (ragged tails are masked).  stream: a hipStream_t or NULL.
  */
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int B, int H_q, int H_kv, int N_q, int N_k, int d,
@@ -93,7 +98,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *   LSE [B,H_q,N_q] fp32 (may be NULL).
  *   K/V pools [num_pages,page_size,H_kv,d] bf16 (the layout fa_decode_splitkv reads): key j
  *     of sequence b is slot j%page_size of page block_table[b*pages_per_seq + j/page_size].
- *   page_size >= 1, pages_per_seq*page_size >= N_k, N_k < 2^24.  Table contents are not
+ *   page_size >= 1, pages_per_seq >= 0, pages_per_seq*page_size >= N_k, N_k < 2^24 (the table
+ *     may be NULL when N_k = 0).  Table contents are not
  *     checked: an entry outside the pool is undefined behaviour, as in any gather.
  *   d in {64, 128}.  scale > 0.  causal: 0 or 1 (bottom-right).  stream: hipStream_t or NULL.
  */
@@ -123,8 +129,10 @@ size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q);
  *   Q, dO, O [B,H_q,N_q,d] bf16; K, V [B,H_kv,N_k,d] bf16; LSE [B,H_q,N_q] fp32 (from fa_fwd
  *   on the same inputs, natural log; -inf for a row that sees no key).
  *   dQ [B,H_q,N_q,d], dK and dV [B,H_kv,N_k,d]: bf16 (FA_BF16) or fp32 (FA_BF16_IN_FP32_OUT);
- *   every element is written (keys no query sees get 0).
- *   workspace: >= fa_bwd_workspace_bytes(B, H_q, N_q) bytes of device memory, 16-byte aligned.
+ *   every element is written (keys no query sees get 0: with N_q = 0, dK = dV = 0; with
+ *   N_k = 0, dQ = 0).
+ *   workspace: >= fa_bwd_workspace_bytes(B, H_q, N_q) bytes of device memory, 16-byte aligned
+ *   (may be NULL when that is 0).
  *   d in {64, 128}.  scale > 0.  causal: 0 or 1.  stream: hipStream_t or NULL.
  *   The result does not depend on scheduling (no atomics): repeated calls agree bit for bit.
  */
@@ -166,7 +174,7 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  *   block_table == NULL: K/V contiguous [B,H_kv,N_k,d] bf16.
  *   block_table != NULL: K/V pools [num_pages,page_size,H_kv,d] bf16; token j of sequence b
  *     is in page block_table[b*pages_per_seq + j/page_size], slot j%page_size; requires
- *     page_size >= 1 and pages_per_seq*page_size >= N_k.  Table contents are not checked:
+ *     page_size >= 1, pages_per_seq >= 0 and pages_per_seq*page_size >= N_k.  Table contents are not checked:
  *     an entry outside the pool is undefined behaviour, as in any gather.
  *   causal: 0 (every cached key visible) or 1 (bottom-right: query t sees j <= N_k - T + t).
  *   num_splits: >= 1, or 0 for fa_decode_num_splits().  Splits are contiguous key ranges of
@@ -190,7 +198,7 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
  *
  *   O_part [num_splits, rows, d] fp32, LSE_part [num_splits, rows] fp32 (the workspace
  *   layout of fa_decode_splitkv); O [rows, d] in out_dtype (FA_BF16 or FA_FP32);
- *   LSE [rows] fp32 (may be NULL).  num_splits >= 1, rows >= 1, 1 <= d <= 512.
+ *   LSE [rows] fp32 (may be NULL).  num_splits >= 1, rows >= 0, 1 <= d <= 512.
  */
 int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE,
                  int num_splits, int rows, int d, int out_dtype, void* stream);

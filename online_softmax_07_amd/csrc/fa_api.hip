@@ -17,8 +17,12 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// A tensor of zero elements may be passed as NULL; any other must not.
+bool present(const void* p, bool nonempty) { return p != nullptr || !nonempty; }
+
+// Sizes: B, heads and d at least 1; the sequence lengths may be 0 (empty inputs).
 int check_heads(int B, int H_q, int H_kv, int n_q, int n_k, int d) {
-  if (B < 1 || H_q < 1 || H_kv < 1 || n_q < 1 || n_k < 1 || d < 1) return FA_ERR_BAD_SHAPE;
+  if (B < 1 || H_q < 1 || H_kv < 1 || n_q < 0 || n_k < 0 || d < 1) return FA_ERR_BAD_SHAPE;
   if (H_q % H_kv != 0) return FA_ERR_BAD_SHAPE;
   // every element index must fit the 64-bit offsets and every row index a 32-bit int
   if ((long long)B * H_q * n_q > 0x7fffffffLL || (long long)B * H_kv * n_k > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
@@ -35,6 +39,7 @@ int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
   const long long row_chunks = ((long long)(H_q / H_kv) * T + 15) / 16;
   const long long base = (long long)B * H_kv * row_chunks;  // workgroups without splitting
   const long long target = (long long)kNumCU * kDecodeWGPerCU;
+  if (base < 1) return 1;  // no query row
   long long ns = base >= target ? 1 : target / base;
   const long long max_useful = ((long long)N_k + 4 * fa::kDecodeChunk - 1) / (4 * fa::kDecodeChunk);
   if (ns > max_useful) ns = max_useful;  // at least one chunk per wave
@@ -63,7 +68,8 @@ int fa_version(void) { return 102; }
 
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
            int N_q, int N_k, int d, float scale, int causal, int dtype, void* stream) {
-  if (!Q || !K || !V || !O) return FA_ERR_NULL_PTR;
+  if (!present(Q, N_q > 0) || !present(O, N_q > 0) || !present(K, N_k > 0) || !present(V, N_k > 0))
+    return FA_ERR_NULL_PTR;
   int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
   if (st != FA_OK) return st;
   if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
@@ -71,6 +77,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   if (dtype != FA_BF16 && dtype != FA_FP32 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)))
     return FA_ERR_ALIGNMENT;
+  if (N_q == 0) return FA_OK;  // no query row: nothing to write (N_k == 0: every row gets O = 0, LSE = -inf)
   fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
   if (dtype == FA_FP32) return status_of(fa::launch_fwd_fp32(a));
   return status_of(fa::launch_fwd_bf16(a, dtype == FA_BF16_IN_FP32_OUT));
@@ -79,39 +86,47 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
 int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
                  int N_q, int N_k, int d, float scale, int causal, const int32_t* block_table, int page_size,
                  int pages_per_seq, int dtype, void* stream) {
-  if (!Q || !K || !V || !O || !block_table) return FA_ERR_NULL_PTR;
+  if (!present(Q, N_q > 0) || !present(O, N_q > 0) || !present(K, N_k > 0) || !present(V, N_k > 0) ||
+      !present(block_table, N_k > 0))
+    return FA_ERR_NULL_PTR;
   int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
   if (st != FA_OK) return st;
   if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
-  if (page_size < 1 || pages_per_seq < 1 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
+  if (page_size < 1 || pages_per_seq < 0 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
   if ((long long)B * pages_per_seq > 0x7fffffffLL || N_k >= (1 << 24)) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)) ||
       !aligned4(block_table))
     return FA_ERR_ALIGNMENT;
+  if (N_q == 0) return FA_OK;
   fa::FwdArgs a{Q, K, V, O, LSE, B, H_q, H_kv, N_q, N_k, d, scale, causal, stream};
   return status_of(fa::launch_fwd_bf16_paged(a, dtype == FA_BF16_IN_FP32_OUT, block_table, page_size, pages_per_seq));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q) {
-  if (B < 1 || H_q < 1 || N_q < 1 || (long long)B * H_q * N_q > 0x7fffffffLL) return 0;
+  if (B < 1 || H_q < 1 || N_q < 1 || (long long)B * H_q * N_q > 0x7fffffffLL) return 0;  // N_q = 0: none
   return fa::bwd_workspace_bytes(B, H_q, N_q);
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE, void* dQ,
            void* dK, void* dV, int B, int H_q, int H_kv, int N_q, int N_k, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL_PTR;
+  const bool hq = N_q > 0, hk = N_k > 0;
+  if (!present(Q, hq) || !present(O, hq) || !present(dO, hq) || !present(LSE, hq) || !present(dQ, hq) ||
+      !present(K, hk) || !present(V, hk) || !present(dK, hk) || !present(dV, hk))
+    return FA_ERR_NULL_PTR;
   int st = check_heads(B, H_q, H_kv, N_q, N_k, d);
   if (st != FA_OK) return st;
   if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1)) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < fa::bwd_workspace_bytes(B, H_q, N_q)) return FA_ERR_WORKSPACE;
+  const size_t need = N_q > 0 ? fa::bwd_workspace_bytes(B, H_q, N_q) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned4(LSE) ||
       !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
     return FA_ERR_ALIGNMENT;
+  if (N_q == 0 && N_k == 0) return FA_OK;
   fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H_q, H_kv, N_q, N_k, d, scale, causal, workspace, stream};
   return status_of(fa::launch_bwd(a, dtype == FA_BF16_IN_FP32_OUT));
 }
@@ -133,12 +148,13 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
                       int H_kv, int T, int N_k, int d, float scale, int causal, int num_splits,
                       const int32_t* block_table, int page_size, int pages_per_seq, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream) {
-  if (!Q || !K || !V || !O) return FA_ERR_NULL_PTR;
+  if (!present(Q, T > 0) || !present(O, T > 0) || !present(K, N_k > 0) || !present(V, N_k > 0))
+    return FA_ERR_NULL_PTR;
   int st = check_heads(B, H_q, H_kv, T, N_k, d);
   if (st != FA_OK) return st;
   if (!(scale > 0.f) || !isfinite(scale) || (causal != 0 && causal != 1) || num_splits < 0) return FA_ERR_BAD_SHAPE;
   if (block_table != nullptr) {
-    if (page_size < 1 || pages_per_seq < 1 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
+    if (page_size < 1 || pages_per_seq < 0 || (long long)pages_per_seq * page_size < N_k) return FA_ERR_BAD_SHAPE;
     if ((long long)B * pages_per_seq > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
   }
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -151,6 +167,7 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
   const size_t need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGNMENT;
+  if (T == 0) return FA_OK;  // no query: nothing to write (N_k == 0: O = 0, LSE = -inf)
 
   const size_t rows = (size_t)B * H_q * T;
   float* O_part = nullptr;
@@ -170,11 +187,12 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
 
 int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE, int num_splits, int rows,
                  int d, int out_dtype, void* stream) {
-  if (!O_part || !LSE_part || !O) return FA_ERR_NULL_PTR;
-  if (num_splits < 1 || rows < 1 || d < 1 || d > 512) return FA_ERR_BAD_SHAPE;
+  if (!present(O_part, rows > 0) || !present(LSE_part, rows > 0) || !present(O, rows > 0)) return FA_ERR_NULL_PTR;
+  if (num_splits < 1 || rows < 0 || d < 1 || d > 512) return FA_ERR_BAD_SHAPE;
   if ((long long)num_splits * rows > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
   if (out_dtype != FA_BF16 && out_dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
   if (!aligned4(O_part) || !aligned4(LSE_part) || !aligned4(O) || (LSE && !aligned4(LSE))) return FA_ERR_ALIGNMENT;
+  if (rows == 0) return FA_OK;
   return status_of(fa::launch_lse_merge(O_part, LSE_part, O, LSE, num_splits, rows, d, out_dtype == FA_FP32, stream));
 }
 

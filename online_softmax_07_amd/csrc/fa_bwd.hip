@@ -527,10 +527,12 @@ hipError_t launch_bwd_main(const BwdArgs& a) {
     const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;
     const long long total = (long long)a.B * a.H_q * n_units;
     if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, BC, NW, CAUSAL, OutT>), dim3((unsigned)total), dim3(64 * NW), 0, st,
-                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO, rec,
-                       (OutT*)a.dQ, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale, scale_log2, n_qblocks, n_units,
-                       (int)total);
+    if (total > 0) {  // N_q = 0: no dQ
+      hipLaunchKernelGGL((bwd_dq_kernel<D, BC, NW, CAUSAL, OutT>), dim3((unsigned)total), dim3(64 * NW), 0, st,
+                         (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO, rec,
+                         (OutT*)a.dQ, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale, scale_log2, n_qblocks, n_units,
+                         (int)total);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -538,6 +540,7 @@ hipError_t launch_bwd_main(const BwdArgs& a) {
   const int n_units = CAUSAL ? (n_kblocks + 1) / 2 : n_kblocks;
   const long long total = (long long)a.B * a.H_kv * n_units;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (total == 0) return hipSuccess;  // N_k = 0: no dK, dV
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OutT>), dim3((unsigned)total), dim3(kThreads), 0, st,
                      (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (const __bf16*)a.dO, rec,
                      (OutT*)a.dK, (OutT*)a.dV, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale, scale_log2, n_kblocks,
@@ -552,9 +555,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool out_f32) {
   const long long threads = n_slots * (D / 8);
   const long long grid = (threads + kThreads - 1) / kThreads;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)a.stream,
-                     (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, static_cast<float*>(a.workspace), a.N_q,
-                     n_rblk, n_slots);
+  if (grid > 0) {  // N_q = 0: no records (dK, dV are then all zero)
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)a.stream,
+                       (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, static_cast<float*>(a.workspace), a.N_q,
+                       n_rblk, n_slots);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.causal)

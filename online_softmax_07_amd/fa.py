@@ -163,9 +163,9 @@ def _paged_sizes(q, k, block_table, n_k, check_table):
     _need(block_table.is_contiguous(), "block_table must be contiguous")
     pages_per_seq = block_table.shape[1]
     N_k = pages_per_seq * page_size if n_k is None else int(n_k)
-    _need(1 <= N_k <= pages_per_seq * page_size, "n_k exceeds the block table")
+    _need(0 <= N_k <= pages_per_seq * page_size, "n_k exceeds the block table")
     _check_dev(q.device, block_table=block_table)
-    if check_table:
+    if check_table and block_table.numel() > 0:
         lo, hi = int(block_table.min()), int(block_table.max())
         _need(0 <= lo and hi < num_pages, f"block_table entries must lie in [0, {num_pages})")
     return H_kv, N_k, page_size, pages_per_seq

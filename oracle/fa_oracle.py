@@ -305,6 +305,8 @@ def attention_head_backward(q, k, v, do, scale: float, causal: bool, o=None, row
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    if n_k == 0:  # no key: every row sees nothing, O = 0 does not depend on q
+        return dq, dk, dv
     for r0 in range(0, n_q, row_chunk):
         r = np.arange(r0, min(n_q, r0 + row_chunk))
         x = scale * (q[r] @ k.T)

@@ -68,7 +68,7 @@ def fwd(**kw):
     (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(K=None), fa.FA_ERR_NULL_PTR), (dict(V=None), fa.FA_ERR_NULL_PTR),
     (dict(O=None), fa.FA_ERR_NULL_PTR),
     (dict(B=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=0), fa.FA_ERR_BAD_SHAPE), (dict(H_kv=0), fa.FA_ERR_BAD_SHAPE),
-    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-3), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(N_q=-1), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-3), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
     (dict(H_q=3, H_kv=2), fa.FA_ERR_BAD_SHAPE), (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=float("inf")), fa.FA_ERR_BAD_SHAPE), (dict(causal=2), fa.FA_ERR_BAD_SHAPE),
@@ -91,9 +91,9 @@ def fwd_paged(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(V=None), fa.FA_ERR_NULL_PTR), (dict(bt=None), fa.FA_ERR_NULL_PTR),
-    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(N_q=-1), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-1), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE), (dict(causal=3), fa.FA_ERR_BAD_SHAPE),
-    (dict(ps=0), fa.FA_ERR_BAD_SHAPE), (dict(pps=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(ps=0), fa.FA_ERR_BAD_SHAPE), (dict(pps=0), fa.FA_ERR_BAD_SHAPE), (dict(pps=-1, N_k=0), fa.FA_ERR_BAD_SHAPE),
     (dict(pps=6), fa.FA_ERR_BAD_SHAPE),                       # 6 * 16 < 100 keys
     (dict(N_k=1 << 24, pps=1 << 20), fa.FA_ERR_BAD_SHAPE),    # beyond the exact page division
     (dict(B=1 << 16, pps=1 << 16, N_k=16), fa.FA_ERR_BAD_SHAPE),  # table entries beyond int32
@@ -117,7 +117,7 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR), (dict(dO=None), fa.FA_ERR_NULL_PTR),
     (dict(L=None), fa.FA_ERR_NULL_PTR), (dict(dK=None), fa.FA_ERR_NULL_PTR), (dict(dV=None), fa.FA_ERR_NULL_PTR),
-    (dict(N_q=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(N_q=-2), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-1), fa.FA_ERR_BAD_SHAPE), (dict(H_q=3), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=-0.1), fa.FA_ERR_BAD_SHAPE), (dict(causal=2), fa.FA_ERR_BAD_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE),
@@ -148,7 +148,7 @@ def dec(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR),
-    (dict(T=0), fa.FA_ERR_BAD_SHAPE), (dict(N_k=0), fa.FA_ERR_BAD_SHAPE), (dict(H_q=5), fa.FA_ERR_BAD_SHAPE),
+    (dict(T=-1), fa.FA_ERR_BAD_SHAPE), (dict(N_k=-1), fa.FA_ERR_BAD_SHAPE), (dict(H_q=5), fa.FA_ERR_BAD_SHAPE),
     (dict(ns=-1), fa.FA_ERR_BAD_SHAPE), (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE), (dict(causal=-1), fa.FA_ERR_BAD_SHAPE),
     (dict(bt=P, ps=0, pps=7), fa.FA_ERR_BAD_SHAPE), (dict(bt=P, ps=16, pps=0), fa.FA_ERR_BAD_SHAPE),
     (dict(bt=P, ps=16, pps=6), fa.FA_ERR_BAD_SHAPE),   # 6 * 16 < 100 keys
@@ -164,7 +164,7 @@ def test_decode_rejects(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(Op=None), fa.FA_ERR_NULL_PTR), (dict(Lp=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR),
-    (dict(ns=0), fa.FA_ERR_BAD_SHAPE), (dict(rows=0), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(ns=0), fa.FA_ERR_BAD_SHAPE), (dict(rows=-1), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),
     (dict(d=513), fa.FA_ERR_BAD_SHAPE), (dict(dtype=fa.FA_BF16_IN_FP32_OUT), fa.FA_ERR_UNSUPPORTED),
     (dict(Op=P + 1), fa.FA_ERR_ALIGNMENT),
 ])
@@ -175,13 +175,38 @@ def test_merge_rejects(kw, status):
                                  a["stream"]) == status
 
 
+def test_empty_calls_enqueue_nothing():
+    """Zero query rows: every entry point validates and returns FA_OK without a HIP call (so
+    this runs on a CPU-only host), and tensors of zero elements may be NULL."""
+    assert fwd(N_q=0) == fa.FA_OK
+    assert fwd(N_q=0, Q=None, O=None) == fa.FA_OK
+    assert fwd(N_q=0, N_k=0, Q=None, O=None, K=None, V=None) == fa.FA_OK
+    assert fwd(N_q=0, dtype=fa.FA_FP32) == fa.FA_OK
+    assert fwd(N_q=1, Q=None) == fa.FA_ERR_NULL_PTR         # a non-empty tensor may not be NULL
+    assert fwd(N_q=0, N_k=5, K=None) == fa.FA_ERR_NULL_PTR
+    assert fwd_paged(N_q=0) == fa.FA_OK
+    assert fwd_paged(N_q=0, N_k=0, bt=None, pps=0, K=None, V=None) == fa.FA_OK
+    assert dec(T=0) == fa.FA_OK
+    assert dec(T=0, Q=None, O=None, LSE=None) == fa.FA_OK
+    assert dec(T=0, N_k=0, K=None, V=None, ns=1, ws=None, wsb=0) == fa.FA_OK
+    assert bwd(N_q=0, N_k=0, Q=None, O=None, dO=None, L=None, dQ=None, K=None, V=None, dK=None, dV=None,
+               ws=None, wsb=0) == fa.FA_OK
+    assert fa.lib().fa_lse_merge(None, None, None, None, 4, 0, 128, fa.FA_BF16, None) == fa.FA_OK
+    # the split heuristic and workspace sizes accept empty lengths
+    assert fa.fa_decode_num_splits(1, 8, 1, 0, 100, 128) == 1
+    assert fa.fa_decode_num_splits(1, 8, 1, 1, 0, 128) == 1
+    assert fa.fa_decode_workspace_bytes(1, 8, 1, 1, 0, 128, 0) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 8, 0) == 0
+
+
 def test_workspace_and_split_sizes():
     # one split needs no workspace
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 1) == 0
     # ns partial rows of d fp32 plus ns lse values, each part rounded to 256 bytes
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == 8 * 32 * 128 * 4 + 1024
     assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == 4 * 512 * 128 * 4 + 4 * 512 * 4
-    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 0
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 8 * 32 * 128 * 4 + 1024  # empty cache, 8 splits
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, -1, 128, 8) == 0                      # invalid length
     # the automatic split count aims at one wave of one workgroup on each of 256 CUs
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 131072, 128) == 32
     assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 4
