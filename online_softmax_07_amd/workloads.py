@@ -138,6 +138,18 @@ def decode(B, H_q, H_kv, T, N_k, d, seed, causal=True, page_size=0, num_pages=No
                   page_size, list(num_splits))
 
 
+def prefill_on_device(B, H_q, H_kv, N_q, N_k, d, seed, device, causal=True, name="prefill_device") -> Prefill:
+    """Q, K, V iid N(0,1) in bf16 drawn directly on `device` by torch's seeded generator, for
+    inputs too large to draw on the host (element offsets past 2^31).  Both sides still see
+    the same bits: tests copy the heads they check to the host for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.randn((B, H_q, N_q, d), generator=g, device=device, dtype=torch.bfloat16)
+    k = torch.randn((B, H_kv, N_k, d), generator=g, device=device, dtype=torch.bfloat16)
+    v = torch.randn((B, H_kv, N_k, d), generator=g, device=device, dtype=torch.bfloat16)
+    return Prefill(name, q, k, v, 1.0 / math.sqrt(d), causal)
+
+
 def grad_output(shape, seed) -> torch.Tensor:
     """The upstream gradient dO for a backward step: iid N(0,1) rounded to bf16, from its
     own seeded stream (so the forward inputs are the same with and without it)."""
