@@ -9,9 +9,10 @@
 // chain "The online softmax on numbers"), and the per-row LSE written once.
 //
 // MI355X mapping:
-//   * 8 (or 4) waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T, with the
-//     32x32x16 bf16 MFMA: K (from LDS) is the A operand, the wave's Q rows (registers,
-//     loaded once) the B operand.  In the accumulator layout each lane owns ONE query row
+//   * d = 128: 8 waves x 32 query rows; d = 64: 4 waves x 64 rows, as two 32-row halves
+//     that share every K and V fragment read from LDS.  Scores are computed transposed,
+//     S^T = K Q^T, with the 32x32x16 bf16 MFMA: K (from LDS) is the A operand, the wave's
+//     Q rows (registers, loaded once) the B operand.  In the accumulator layout each lane owns ONE query row
 //     (lane % 32) and 16 keys per 32-key block, so the row max is a register reduction
 //     plus one exchange between the two wave halves, the row sum stays a per-lane partial
 //     until the end, and the rescale factor is a per-lane scalar.
@@ -43,14 +44,15 @@
 
 namespace fa {
 
-// NW waves of 32 query rows per workgroup.  The launches mostly use NW = 8 (BR = 256, one
-// workgroup and two waves per SIMD on each CU): every K/V tile staged in LDS serves 256 rows,
-// and the LDS freed by the second workgroup holds 128-key tiles at d = 128.
+// NW waves of RH x 32 query rows per workgroup, BR = 256 rows in both launches, two waves
+// per SIMD on each CU (one 8-wave workgroup at d = 128, two 4-wave ones at d = 64): every
+// K/V tile staged in LDS serves 256 rows, and at d = 128 the LDS a second workgroup would
+// take holds 128-key tiles instead.
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
 
-template <int D, int BC, int NW>
+template <int D, int BC, int NW, int RH>
 struct FwdTile {
-  static constexpr int BR = 32 * NW;        // query rows per workgroup
+  static constexpr int BR = 32 * NW * RH;   // query rows per workgroup (RH 32-row halves per wave)
   static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
   static constexpr int STAGE = BC * D;      // elements of one K or V stage (no padding)
   static constexpr int ROWS_PER_DMA = 1024 / (2 * D);   // rows one wave-wide 16-byte DMA fills
@@ -66,13 +68,13 @@ struct FwdTile {
   }
 };
 
-template <int D, int BC, int NW, bool CAUSAL, bool PAGED, typename OutT>
+template <int D, int BC, int NW, int RH, bool CAUSAL, bool PAGED, typename OutT>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
     float scale_log2, int n_qblocks, int n_units, int total_wg,
     const int32_t* __restrict__ block_table, int page_size, int pages_per_seq, float inv_page_size) {
-  using T = FwdTile<D, BC, NW>;
+  using T = FwdTile<D, BC, NW, RH>;
   // Two K and two V stages as separate arrays: with the stage known at compile time the
   // compiler can tell that a tile's LDS reads do not touch the stage being refilled, and
   // does not wait for the refill before reading.
@@ -120,18 +122,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   for (int pass = 0; pass < n_pass; ++pass) {
     const int qb = !CAUSAL ? unit : (pass == 0 ? n_qblocks - 1 - unit : unit);
     const int q0 = qb * T::BR;
-    const int wave_row0 = q0 + wave * 32;
-    const int qrow = wave_row0 + l32;
+    const int wave_row0 = q0 + wave * 32 * RH;
+    int qrow[RH];  // this lane's row in each 32-row half of the wave
+#pragma unroll
+    for (int x = 0; x < RH; ++x) qrow[x] = wave_row0 + 32 * x + l32;
     const int shift = N_k - N_q;   // bottom-right alignment: row i sees keys j <= i + shift
 
     // ---- Q block: read once, kept as MFMA B fragments ----
-    bf16x8 qf[D / 16];
-    {
-      const int qr = qrow < N_q ? qrow : N_q - 1;  // clamped row; zeroed below
+    bf16x8 qf[RH][D / 16];
+#pragma unroll
+    for (int x = 0; x < RH; ++x) {
+      const int qr = qrow[x] < N_q ? qrow[x] : N_q - 1;  // clamped row; zeroed below
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        qf[t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qr * D + 16 * t + 8 * hh);
-        if (qrow >= N_q) qf[t] = bf16x8{};
+        qf[x][t] = *reinterpret_cast<const bf16x8*>(Qp + (size_t)qr * D + 16 * t + 8 * hh);
+        if (qrow[x] >= N_q) qf[x][t] = bf16x8{};
       }
     }
 
@@ -141,16 +146,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
       const int max_key = min(q0 + T::BR - 1, N_q - 1) + shift;
       n_tiles = max_key < 0 ? 0 : min(n_tiles, max_key / BC + 1);
     }
-    const int wave_last_key = min(wave_row0 + 31, N_q - 1) + shift;  // causal reach of this wave
-    const int row_lim = CAUSAL ? min(N_k - 1, qrow + shift) : N_k - 1; // last key this row sees
-
-    // ---- carries ----
-    float m_run = kNegInf;  // reference max (log2 units of the scaled scores)
-    float l_run = 0.f;      // this lane's partial sum of p over its keys (fp32 p: for the LSE)
-    float lb_run = 0.f;     // the same sum over the bf16-rounded p the PV product uses (for O)
-    f32x16 o[T::NCB];
+    const int wave_last_key = min(wave_row0 + 32 * RH - 1, N_q - 1) + shift;  // causal reach of this wave
+    int row_lim[RH];  // last key each of this lane's rows sees
 #pragma unroll
-    for (int cb = 0; cb < T::NCB; ++cb) o[cb] = f32x16{};
+    for (int x = 0; x < RH; ++x) row_lim[x] = CAUSAL ? min(N_k - 1, qrow[x] + shift) : N_k - 1;
+
+    // ---- carries, per row half ----
+    float m_run[RH];   // reference max (log2 units of the scaled scores)
+    float l_run[RH];   // this lane's partial sum of p over its keys (fp32 p: for the LSE)
+    float lb_run[RH];  // the same sum over the bf16-rounded p the PV product uses (for O)
+    f32x16 o[RH][T::NCB];
+#pragma unroll
+    for (int x = 0; x < RH; ++x) {
+      m_run[x] = kNegInf;
+      l_run[x] = 0.f;
+      lb_run[x] = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < T::NCB; ++cb) o[x][cb] = f32x16{};
+    }
 
     // ---- K/V staging: global -> LDS directly (16-byte buffer loads with an LDS target) ----
     // Wave w's DMA i fills rows ROWS_PER_DMA * (DMA * w + i) + lane / CHUNKS; the lane fetches
@@ -261,9 +274,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
       if (!CAUSAL || kbase <= wave_last_key) {
         // ---- S^T = K_j Q^T: NKB independent accumulators, fragments read one step ahead ----
         __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
-        f32x16 s[T::NKB];
+        f32x16 s[RH][T::NKB];
 #pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb) s[kb] = f32x16{};
+        for (int x = 0; x < RH; ++x)
+#pragma unroll
+          for (int kb = 0; kb < T::NKB; ++kb) s[x][kb] = f32x16{};
         bf16x8 kf[2][T::NKB];
 #pragma unroll
         for (int kb = 0; kb < T::NKB; ++kb)
@@ -277,7 +292,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
                   *reinterpret_cast<const bf16x8*>(ks + kb * 32 * D + koff[t + 1]);
           }
 #pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb) s[kb] = mfma32x32x16(kf[t & 1][kb], qf[t], s[kb]);
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int x = 0; x < RH; ++x) s[x][kb] = mfma32x32x16(kf[t & 1][kb], qf[x][t], s[x][kb]);
 #pragma unroll
           for (int i = t * DMA_PER_STEP; i < (t + 1) * DMA_PER_STEP && i < NDMA; ++i)
             dma(i, j + 1, kr_next, vr_next, pg_next, ks_next, vs_next);
@@ -286,57 +303,60 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::NKB, 0);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, T::NKB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, T::NKB * RH, 0);
           if (t * DMA_PER_STEP < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, DMA_PER_STEP, 0);
           if (t + 2 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, T::NKB, 0);
         }
 
         __builtin_amdgcn_s_setprio(0);
-        // ---- mask: ragged tail and the bottom-right causal edge ----
-        const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + shift);
-        if (need_mask) {
-          const int thr = row_lim - kbase - 4 * hh;  // key offset in this lane's numbering
+        bf16x8 pf[RH][BC / 16];
+#pragma unroll
+        for (int x = 0; x < RH; ++x) {
+          // ---- mask: ragged tail and the bottom-right causal edge ----
+          const bool need_mask = (kbase + BC > N_k) || (CAUSAL && kbase + BC - 1 > wave_row0 + 32 * x + shift);
+          if (need_mask) {
+            const int thr = row_lim[x] - kbase - 4 * hh;  // key offset in this lane's numbering
+#pragma unroll
+            for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (kb * 32 + 8 * (r >> 2) + (r & 3) > thr) s[x][kb][r] = kNegInf;
+          }
+
+          // ---- online softmax (base 2, lazily rescaled) ----
+          float mx = kNegInf;
 #pragma unroll
           for (int kb = 0; kb < T::NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kb * 32 + 8 * (r >> 2) + (r & 3) > thr) s[kb][r] = kNegInf;
-        }
-
-        // ---- online softmax (base 2, lazily rescaled) ----
-        float mx = kNegInf;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[x][kb][r]);
+          mx = max_halves(mx) * scale_log2;
+          if (wave_any(mx > m_run[x] + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run[x], mx);
+            // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
+            const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run[x] - m_new);
+            l_run[x] *= alpha;
+            lb_run[x] *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx) * scale_log2;
-        if (wave_any(mx > m_run + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run, mx);
-          // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
-          const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run - m_new);
-          l_run *= alpha;
-          lb_run *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < T::NCB; ++cb) o[cb] *= alpha;
-          m_run = m_new;
-        }
-        const float m_use = m_run == kNegInf ? 0.f : m_run;  // a row with no key yet: all p = 0
-#pragma unroll
-        for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[kb][r] = exp2f_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-            l_run += s[kb][r];
+            for (int cb = 0; cb < T::NCB; ++cb) o[x][cb] *= alpha;
+            m_run[x] = m_new;
           }
-        // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
-        bf16x8 pf[BC / 16];
+          const float m_use = m_run[x] == kNegInf ? 0.f : m_run[x];  // a row with no key yet: all p = 0
 #pragma unroll
-        for (int u = 0; u < BC / 16; ++u) {
-          const f32x16& sk = s[u >> 1];
-          const int r0 = (u & 1) * 8;
-          pf[u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
-                                  sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
-          lb_run = sum_bf16x8(pf[u], lb_run);
+          for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              s[x][kb][r] = exp2f_hw(__builtin_fmaf(s[x][kb][r], scale_log2, -m_use));
+              l_run[x] += s[x][kb][r];
+            }
+          // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
+#pragma unroll
+          for (int u = 0; u < BC / 16; ++u) {
+            const f32x16& sk = s[x][u >> 1];
+            const int r0 = (u & 1) * 8;
+            pf[x][u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
+                                       sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
+            lb_run[x] = sum_bf16x8(pf[x][u], lb_run[x]);
+          }
         }
 
         // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
@@ -355,7 +375,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
             for (int cb = 0; cb < T::NCB; ++cb) vf[(u + 1) & 1][cb] = vfrag(u + 1, cb);
           }
 #pragma unroll
-          for (int cb = 0; cb < T::NCB; ++cb) o[cb] = mfma32x32x16(vf[u & 1][cb], pf[u], o[cb]);
+          for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+            for (int x = 0; x < RH; ++x) o[x][cb] = mfma32x32x16(vf[u & 1][cb], pf[x][u], o[x][cb]);
         }
         __builtin_amdgcn_s_setprio(0);
       } else {
@@ -375,41 +397,47 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     }
 
     // ---- epilogue: one division, O and LSE written once ----
-    const float l_tot = l_run + shfl_xor_f(l_run, 32);  // the two wave halves hold one row's keys
-    const float lb_tot = lb_run + shfl_xor_f(lb_run, 32);
-    if (qrow < N_q) {
-    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
-    OutT* Orow = O + ((size_t)bh * N_q + qrow) * D;
 #pragma unroll
-    for (int cb = 0; cb < T::NCB; ++cb)
+    for (int x = 0; x < RH; ++x) {
+      const float l_tot = l_run[x] + shfl_xor_f(l_run[x], 32);  // the two wave halves hold one row's keys
+      const float lb_tot = lb_run[x] + shfl_xor_f(lb_run[x], 32);
+      if (qrow[x] < N_q) {
+        const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+        OutT* Orow = O + ((size_t)bh * N_q + qrow[x]) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = cb * 32 + 8 * g + 4 * hh;
-        const f32x4 v = {o[cb][4 * g] * inv, o[cb][4 * g + 1] * inv, o[cb][4 * g + 2] * inv,
-                         o[cb][4 * g + 3] * inv};
-        if constexpr (sizeof(OutT) == 4) {
-          *reinterpret_cast<f32x4*>(Orow + c) = v;
-        } else {
-          *reinterpret_cast<bf16x4*>(Orow + c) = __builtin_convertvector(v, bf16x4);
+        for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = cb * 32 + 8 * g + 4 * hh;
+            const f32x4 v = {o[x][cb][4 * g] * inv, o[x][cb][4 * g + 1] * inv, o[x][cb][4 * g + 2] * inv,
+                             o[x][cb][4 * g + 3] * inv};
+            if constexpr (sizeof(OutT) == 4) {
+              *reinterpret_cast<f32x4*>(Orow + c) = v;
+            } else {
+              *reinterpret_cast<bf16x4*>(Orow + c) = __builtin_convertvector(v, bf16x4);
+            }
+          }
+        if (LSE != nullptr && hh == 0) {
+          LSE[(size_t)bh * N_q + qrow[x]] = l_tot > 0.f ? (m_run[x] + log2f_hw(l_tot)) * kLn2 : kNegInf;
         }
       }
-    if (LSE != nullptr && hh == 0) {
-      LSE[(size_t)bh * N_q + qrow] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
-    }
     }
   }
 }
 
 template <int D, int BC, bool CAUSAL, bool PAGED, typename OutT>
 static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_size, int pages_per_seq) {
-  // 8 waves; 4 (two 128-row workgroups per CU) measured 1-5 % slower, except causal d = 64
-  constexpr int NW = (D == 64 && CAUSAL && !PAGED) ? 4 : 8;
-  constexpr int BR = FwdTile<D, BC, NW>::BR;
+  // d = 128: 8 waves of 32 rows (4 waves measured 1-5 % slower).  d = 64: 4 waves of two
+  // 32-row halves, so each K or V fragment read from LDS feeds two MFMAs; the registers
+  // this takes fit at d = 64 only
+  constexpr int RH = D == 64 ? 2 : 1;
+  constexpr int NW = RH == 2 ? 4 : 8;
+  constexpr int BR = FwdTile<D, BC, NW, RH>::BR;
   const int n_qblocks = (a.N_q + BR - 1) / BR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
   const long long total = (long long)a.B * a.H_q * n_units;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, CAUSAL, PAGED, OutT>), dim3((unsigned)total), dim3(64 * NW), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RH, CAUSAL, PAGED, OutT>), dim3((unsigned)total), dim3(64 * NW), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (OutT*)a.O, a.LSE, a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e, n_qblocks,
                      n_units, (int)total, block_table, page_size, pages_per_seq,
@@ -417,25 +445,26 @@ static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_
   return hipGetLastError();
 }
 
-template <int D, int BC, bool PAGED>
+template <int D, bool PAGED>
 static hipError_t dispatch_out(const FwdArgs& a, bool out_f32, const int32_t* bt, int ps, int pps) {
-  // d = 128: 128-key tiles (half the barriers per key) for contiguous K/V; the paged variant
-  // keeps 64-key tiles, whose per-lane page addressing would not fit the registers otherwise
-  constexpr int BC2 = (D == 128 && !PAGED) ? 128 : BC;
+  // key tile: 128 keys for contiguous K/V at d = 128 (half the barriers per key); 64 keys for
+  // the paged variant at d = 128 (its per-lane page addressing would not fit the registers
+  // otherwise) and at d = 64 (two row halves per wave)
+  constexpr int BC = (D == 128 && !PAGED) ? 128 : 64;
   if (a.causal)
-    return out_f32 ? launch<D, BC2, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC2, true, PAGED, __bf16>(a, bt, ps, pps);
-  return out_f32 ? launch<D, BC2, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC2, false, PAGED, __bf16>(a, bt, ps, pps);
+    return out_f32 ? launch<D, BC, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC, true, PAGED, __bf16>(a, bt, ps, pps);
+  return out_f32 ? launch<D, BC, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC, false, PAGED, __bf16>(a, bt, ps, pps);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool out_f32) {
-  if (a.d == 128) return dispatch_out<128, 64, false>(a, out_f32, nullptr, 0, 0);
-  return dispatch_out<64, 128, false>(a, out_f32, nullptr, 0, 0);
+  if (a.d == 128) return dispatch_out<128, false>(a, out_f32, nullptr, 0, 0);
+  return dispatch_out<64, false>(a, out_f32, nullptr, 0, 0);
 }
 
 hipError_t launch_fwd_bf16_paged(const FwdArgs& a, bool out_f32, const int32_t* block_table, int page_size,
                                  int pages_per_seq) {
-  if (a.d == 128) return dispatch_out<128, 64, true>(a, out_f32, block_table, page_size, pages_per_seq);
-  return dispatch_out<64, 128, true>(a, out_f32, block_table, page_size, pages_per_seq);
+  if (a.d == 128) return dispatch_out<128, true>(a, out_f32, block_table, page_size, pages_per_seq);
+  return dispatch_out<64, true>(a, out_f32, block_table, page_size, pages_per_seq);
 }
 
 }  // namespace fa
