@@ -211,9 +211,9 @@ def main():
         ms_per_step = total_ms / args.steps
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit, bound, peak, achieved = "TFLOP/s", "mfma", rl.PEAK_BF16_MFMA_TFLOPS, flops / (avg * 1e-3) / 1e12
-        bc = 64 if (s["d"] == 128 and paged) else 128       # the launch's key tile
-        nw = 4 if (s["d"] == 64 and w.causal and not paged) else 8   # and waves per workgroup
-        kernel = (f"fa::fwd_bf16_kernel<{s['d']}, {bc}, {nw}, {str(w.causal).lower()}, "
+        bc = 128 if (s["d"] == 128 and not paged) else 64   # the launch's key tile,
+        nw, rh = (8, 1) if s["d"] == 128 else (4, 2)          # waves and 32-row halves per wave
+        kernel = (f"fa::fwd_bf16_kernel<{s['d']}, {bc}, {nw}, {rh}, {str(w.causal).lower()}, "
                   f"{str(paged).lower()}, bf16>")
         if head in BACKWARD:
             kernel = "fa::bwd_prep_kernel + fa::bwd_dq_kernel + fa::bwd_dkdv_kernel (whole fa_bwd call)"

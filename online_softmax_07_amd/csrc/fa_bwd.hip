@@ -26,6 +26,8 @@
 //     written once: no atomics, and the result does not depend on scheduling.
 // Both main kernels walk only the tiles the bottom-right causal mask leaves visible, and a
 // causal workgroup takes a heavy and a light block of one head so all cost the same.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -91,6 +93,16 @@ struct OperandOffsets {
       }
   }
 };
+
+// Calls f(std::integral_constant<int, i>) for i = I .. N-1: a loop whose index is a
+// compile-time constant in the body, so register arrays are never indexed dynamically.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Transposed operand of a 16-row step starting at `row0` of an LDS tile: rows become k.
 template <int D>
@@ -433,21 +445,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();
 
+    // Masking: register i of a 32-row sub-block starting at row qs0 holds row
+    // qs0 + 8(i/4) + 4hh + i%4, which sees this lane's key iff row + shift >= key; with
+    // thr = qs0 + 4hh + shift - key that is 8(i/4) + i%4 + thr >= 0.  Keys past N_k are
+    // never seen.
+    const bool key_ok = key < N_k;
     auto step = [&](int s, const __bf16* qs, const __bf16* gs, const float* rs, __bf16* qs_n, __bf16* gs_n,
                     float* rs_n) {
       issue(s + 1, qs_n, gs_n, rs_n);
       int bh, q0;
       step_rows(s, bh, q0);
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-      const int qs0 = q0 + 32 * sb;  // first row of this sub-block
-      const __bf16* qsb = qs + sb * 32 * D;
-      const __bf16* gsb = gs + sb * 32 * D;
-      const float* rsb = rs + sb * 64;
-      if (!CAUSAL || qs0 + 31 >= wave_first_row) {
-        // S = Q K^T and dP = dO V^T for these 32 rows x this wave's 32 keys
-        __builtin_amdgcn_s_setprio(1);
-        f32x16 sc = f32x16{}, dp = f32x16{};
+      // S = Q K^T and dP = dO V^T for the 32 rows of sub-block sb x this wave's 32 keys
+      auto scores = [&](int sb, f32x16& sc, f32x16& dp) {
+        const __bf16* qsb = qs + sb * 32 * D;
+        const __bf16* gsb = gs + sb * 32 * D;
+        sc = f32x16{};
+        dp = f32x16{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
           const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qsb + off.plain[t]);
@@ -455,11 +468,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           sc = mfma32x32x16(qa, kf[t], sc);
           dp = mfma32x32x16(ga, vf[t], dp);
         }
-        __builtin_amdgcn_s_setprio(0);
-        // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf),
-        // dS = P (dP - D[row]).  Register i holds row 8(i/4) + 4hh + i%4.
-        const bool need_mask = (kw0 + 32 > N_k) || (CAUSAL && kw0 + 31 > qs0 + shift);
-        const int thr = qs0 + 4 * hh + shift - key;  // key visible to row r iff r + thr >= 0
+      };
+      // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf),
+      // dS = P (dP - D[row]), both as bf16 MFMA operands.  Branch-free, so that it can be
+      // interleaved with independent MFMAs.
+      auto softmax = [&](int sb, const f32x16& sc, const f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+        const int qs0 = q0 + 32 * sb;
+        const float* rsb = rs + sb * 64;
+        const int thr = qs0 + 4 * hh + shift - key;
         f32x16 p, ds;
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -469,12 +485,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * gq + e;
             float pv = exp2f_hw(__builtin_fmaf(sc[i], scale_log2, -l4[e]));
-            if (need_mask && (key >= N_k || (CAUSAL && 8 * gq + e + thr < 0))) pv = 0.f;
+            const bool vis = key_ok && (!CAUSAL || 8 * gq + e + thr >= 0);
+            pv = vis ? pv : 0.f;
             p[i] = pv;
             ds[i] = pv * (dp[i] - d4[e]);
           }
         }
-        bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           pf[u] = to_bf16x8(f32x8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3], p[8 * u + 4], p[8 * u + 5],
@@ -482,8 +498,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           dsf[u] = to_bf16x8(f32x8{ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3], ds[8 * u + 4],
                                    ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
         }
-        // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
-        __builtin_amdgcn_s_setprio(1);
+      };
+      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
+      auto grads = [&](int sb, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
+        const __bf16* qsb = qs + sb * 32 * D;
+        const __bf16* gsb = gs + sb * 32 * D;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -491,8 +510,95 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             dv[cb] = mfma32x32x16(tr_frag<D>(gsb, 16 * u, off, cb), pf[u], dv[cb]);
             dk[cb] = mfma32x32x16(tr_frag<D>(qsb, 16 * u, off, cb), dsf[u], dk[cb]);
           }
-        __builtin_amdgcn_s_setprio(0);
-      }
+      };
+      static_assert(NSB == 2, "the step is written for two 32-row sub-blocks");
+      // causal: sub-block rows below wave_first_row see none of this wave's keys
+      if (!CAUSAL || q0 + 31 >= wave_first_row) {
+        // Both sub-blocks, as one software-pipelined stream of MFMAs: the scores (S, dP) of
+        // sub-blocks 0 and 1, then the gradients (dV, dK) of 0 and 1.  Each LDS operand is
+        // read PD MFMAs ahead of its use (one wave per SIMD: nothing else hides the LDS
+        // latency), and the softmax of a sub-block runs in the shadow of the MFMAs that
+        // follow its scores.  A scheduling fence after each slot keeps this order.
+        constexpr int NMS = 2 * (D / 16);  // score MFMAs per sub-block
+        constexpr int NMG = 4 * NCB;       // gradient MFMAs per sub-block
+        constexpr int NMT = 2 * NMS + 2 * NMG;
+        constexpr int PD = 2;
+        constexpr int kRecLead = 3;
+        f32x16 sc[2], dp[2];
+        f32x8 p8, d8;
+        bf16x8 pf[2][2], dsf[2][2];
+        f32x4 l4[2][4], d4[2][4];
+        auto load_op = [&](auto mc) -> bf16x8 {
+          constexpr int m = decltype(mc)::value;
+          if constexpr (m < 2 * NMS) {
+            constexpr int sb = m / NMS, j = m % NMS;
+            return *reinterpret_cast<const bf16x8*>((j & 1 ? gs : qs) + sb * 32 * D + off.plain[j >> 1]);
+          } else {
+            constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
+            return tr_frag<D>((j & 1 ? qs : gs) + sb * 32 * D, 16 * (j / (2 * NCB)), off, (j >> 1) % NCB);
+          }
+        };
+        auto load_rec = [&](int sb, int gq) {
+          l4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 8 * gq + 4 * hh);
+          d4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 32 + 8 * gq + 4 * hh);
+        };
+        // element i of sub-block sb: P and dS (register i holds row 8(i/4) + 4hh + i%4);
+        // every eighth element completes one bf16 operand pair
+        auto soft_elem = [&](int sb, int i) {
+          const int gq = i >> 2, e = i & 3;
+          const int thr = q0 + 32 * sb + 4 * hh + shift - key;
+          float pv = exp2f_hw(__builtin_fmaf(sc[sb][i], scale_log2, -l4[sb][gq][e]));
+          const bool vis = key_ok && (!CAUSAL || 8 * gq + e + thr >= 0);
+          pv = vis ? pv : 0.f;
+          p8[i & 7] = pv;
+          d8[i & 7] = pv * (dp[sb][i] - d4[sb][gq][e]);
+          if ((i & 7) == 7) {
+            pf[sb][i >> 3] = to_bf16x8(p8);
+            dsf[sb][i >> 3] = to_bf16x8(d8);
+          }
+        };
+        sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+        bf16x8 ops[PD];
+        static_for<0, PD>([&](auto mc) { ops[decltype(mc)::value] = load_op(mc); });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NMT>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          const bf16x8 a = ops[m % PD];
+          if constexpr (m + PD < NMT) ops[m % PD] = load_op(std::integral_constant<int, m + PD>{});
+          // the softmax of sub-block sb takes slots [s0, s0 + ns) after its last score MFMA,
+          // element i in slot s0 + i ns / 16; the records of a row group arrive kRecLead
+          // slots before its first element
+          constexpr int s0[2] = {NMS + 2, 2 * NMS + 2}, ns[2] = {NMS - 2, NMG - 2};
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+              if (m == s0[sb] + gq * ns[sb] / 4 - kRecLead) load_rec(sb, gq);
+          if constexpr (m < 2 * NMS) {
+            constexpr int sb = m / NMS, j = m % NMS;
+            if constexpr (j & 1) dp[sb] = mfma32x32x16(a, vf[j >> 1], dp[sb]);
+            else sc[sb] = mfma32x32x16(a, kf[j >> 1], sc[sb]);
+          } else {
+            constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
+            constexpr int u = j / (2 * NCB), cb = (j >> 1) % NCB;
+            if constexpr (j & 1) dk[cb] = mfma32x32x16(a, dsf[sb][u], dk[cb]);
+            else dv[cb] = mfma32x32x16(a, pf[sb][u], dv[cb]);
+          }
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+            if (m >= s0[sb] && m < s0[sb] + ns[sb]) {
+              const int k = m - s0[sb];
+#pragma unroll
+              for (int i = 16 * k / ns[sb]; i < 16 * (k + 1) / ns[sb]; ++i) soft_elem(sb, i);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else if (q0 + 63 >= wave_first_row) {
+        f32x16 sc1, dp1;
+        bf16x8 pf1[2], ds1[2];
+        scores(1, sc1, dp1);
+        softmax(1, sc1, dp1, pf1, ds1);
+        grads(1, pf1, ds1);
       }
       wait_vmem();
       __syncthreads();
