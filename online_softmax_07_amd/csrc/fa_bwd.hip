@@ -518,14 +518,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // sub-blocks 0 and 1, then the gradients (dV, dK) of 0 and 1.  Each LDS operand is
         // read PD MFMAs ahead of its use (one wave per SIMD: nothing else hides the LDS
         // latency), and the softmax of a sub-block runs in the shadow of the MFMAs that
-        // follow its scores.  A scheduling fence after each slot keeps this order.
+        // follow its scores, EPS elements per MFMA slot in two stages (exponential, then
+        // mask and dS) one slot apart, so that each slot's VALU work is independent.  A
+        // scheduling fence after each slot keeps this order.
         constexpr int NMS = 2 * (D / 16);  // score MFMAs per sub-block
         constexpr int NMG = 4 * NCB;       // gradient MFMAs per sub-block
         constexpr int NMT = 2 * NMS + 2 * NMG;
         constexpr int PD = 2;
         constexpr int kRecLead = 3;
+        constexpr int EPS = D >= 128 ? 1 : 2;  // softmax elements per slot
+        constexpr int NSL = 16 / EPS;          // slots of stage 1 per sub-block
+        constexpr int S0[2] = {NMS + 1, 2 * NMS + 1};  // first softmax slot of each sub-block
+        static_assert(S0[0] + 8 / EPS + 1 <= 2 * NMS && S0[0] + NSL + 1 <= 2 * NMS + 2 * NCB &&
+                          S0[1] + 8 / EPS + 1 <= 2 * NMS + NMG && S0[1] + NSL + 1 <= 2 * NMS + NMG + 2 * NCB,
+                      "each bf16 operand pair is complete before its first gradient MFMA");
         f32x16 sc[2], dp[2];
-        f32x8 p8, d8;
+        float ex[2][16];
+        f32x8 p8[2], d8[2];
         bf16x8 pf[2][2], dsf[2][2];
         f32x4 l4[2][4], d4[2][4];
         auto load_op = [&](auto mc) -> bf16x8 {
@@ -542,57 +551,66 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           l4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 8 * gq + 4 * hh);
           d4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 32 + 8 * gq + 4 * hh);
         };
-        // element i of sub-block sb: P and dS (register i holds row 8(i/4) + 4hh + i%4);
-        // every eighth element completes one bf16 operand pair
-        auto soft_elem = [&](int sb, int i) {
-          const int gq = i >> 2, e = i & 3;
-          const int thr = q0 + 32 * sb + 4 * hh + shift - key;
-          float pv = exp2f_hw(__builtin_fmaf(sc[sb][i], scale_log2, -l4[sb][gq][e]));
-          const bool vis = key_ok && (!CAUSAL || 8 * gq + e + thr >= 0);
-          pv = vis ? pv : 0.f;
-          p8[i & 7] = pv;
-          d8[i & 7] = pv * (dp[sb][i] - d4[sb][gq][e]);
+        // register i of a sub-block holds row 8(i/4) + 4hh + i%4 of it
+        auto stage1 = [&](int sb, int i) {  // e = 2^(s scale log2e - lse2[row])
+          ex[sb][i] = exp2f_hw(__builtin_fmaf(sc[sb][i], scale_log2, -l4[sb][i >> 2][i & 3]));
+        };
+        auto stage2 = [&](auto maskc, int sb, int i) {  // P (0 past the mask), dS = P (dP - D[row])
+          float pv = ex[sb][i];
+          if constexpr (decltype(maskc)::value) {
+            const int thr = q0 + 32 * sb + 4 * hh + shift - key;
+            const bool vis = key_ok && (!CAUSAL || 8 * (i >> 2) + (i & 3) + thr >= 0);
+            pv = vis ? pv : 0.f;
+          }
+          p8[sb][i & 7] = pv;
+          d8[sb][i & 7] = pv * (dp[sb][i] - d4[sb][i >> 2][i & 3]);
           if ((i & 7) == 7) {
-            pf[sb][i >> 3] = to_bf16x8(p8);
-            dsf[sb][i >> 3] = to_bf16x8(d8);
+            pf[sb][i >> 3] = to_bf16x8(p8[sb]);
+            dsf[sb][i >> 3] = to_bf16x8(d8[sb]);
           }
         };
-        sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
-        bf16x8 ops[PD];
-        static_for<0, PD>([&](auto mc) { ops[decltype(mc)::value] = load_op(mc); });
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, NMT>([&](auto mc) {
-          constexpr int m = decltype(mc)::value;
-          const bf16x8 a = ops[m % PD];
-          if constexpr (m + PD < NMT) ops[m % PD] = load_op(std::integral_constant<int, m + PD>{});
-          // the softmax of sub-block sb takes slots [s0, s0 + ns) after its last score MFMA,
-          // element i in slot s0 + i ns / 16; the records of a row group arrive kRecLead
-          // slots before its first element
-          constexpr int s0[2] = {NMS + 2, 2 * NMS + 2}, ns[2] = {NMS - 2, NMG - 2};
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-              if (m == s0[sb] + gq * ns[sb] / 4 - kRecLead) load_rec(sb, gq);
-          if constexpr (m < 2 * NMS) {
-            constexpr int sb = m / NMS, j = m % NMS;
-            if constexpr (j & 1) dp[sb] = mfma32x32x16(a, vf[j >> 1], dp[sb]);
-            else sc[sb] = mfma32x32x16(a, kf[j >> 1], sc[sb]);
-          } else {
-            constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
-            constexpr int u = j / (2 * NCB), cb = (j >> 1) % NCB;
-            if constexpr (j & 1) dk[cb] = mfma32x32x16(a, dsf[sb][u], dk[cb]);
-            else dv[cb] = mfma32x32x16(a, pf[sb][u], dv[cb]);
-          }
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb)
-            if (m >= s0[sb] && m < s0[sb] + ns[sb]) {
-              const int k = m - s0[sb];
-#pragma unroll
-              for (int i = 16 * k / ns[sb]; i < 16 * (k + 1) / ns[sb]; ++i) soft_elem(sb, i);
-            }
+        auto stream = [&](auto maskc) {
+          sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+          bf16x8 ops[PD];
+          static_for<0, PD>([&](auto mc) { ops[decltype(mc)::value] = load_op(mc); });
           __builtin_amdgcn_sched_barrier(0);
-        });
+          static_for<0, NMT>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            const bf16x8 a = ops[m % PD];
+            if constexpr (m + PD < NMT) ops[m % PD] = load_op(std::integral_constant<int, m + PD>{});
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq)
+                if (m == S0[sb] + 4 * gq / EPS - kRecLead) load_rec(sb, gq);
+            if constexpr (m < 2 * NMS) {
+              constexpr int sb = m / NMS, j = m % NMS;
+              if constexpr (j & 1) dp[sb] = mfma32x32x16(a, vf[j >> 1], dp[sb]);
+              else sc[sb] = mfma32x32x16(a, kf[j >> 1], sc[sb]);
+            } else {
+              constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
+              constexpr int u = j / (2 * NCB), cb = (j >> 1) % NCB;
+              if constexpr (j & 1) dk[cb] = mfma32x32x16(a, dsf[sb][u], dk[cb]);
+              else dv[cb] = mfma32x32x16(a, pf[sb][u], dv[cb]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+              const int k = m - S0[sb];
+              if (k >= 0 && k < NSL) {
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) stage1(sb, EPS * k + e);
+              }
+              if (k >= 1 && k <= NSL) {
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) stage2(maskc, sb, EPS * (k - 1) + e);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        };
+        // masking only where this wave's keys run past N_k or past the first row's reach
+        if (kw0 + 32 > N_k || (CAUSAL && kw0 + 31 > q0 + shift)) stream(std::true_type{});
+        else stream(std::false_type{});
       } else if (q0 + 63 >= wave_first_row) {
         f32x16 sc1, dp1;
         bf16x8 pf1[2], ds1[2];
