@@ -22,7 +22,9 @@
 //     (of every query head of the GQA group in turn) stream through LDS and are taken in
 //     two 32-row halves.  S = Q K^T and
 //     dP = dO V^T put one key in each lane; dV^T += dO^T P and dK^T += Q^T dS read dO^T
-//     and Q^T with the transposing LDS read.  dK and dV (summed over the group) are
+//     and Q^T with the transposing LDS read.  The kernel runs one wave per SIMD, so each
+//     64-row step is issued as one software-pipelined stream of MFMAs with the operand
+//     reads and the softmax placed between them.  dK and dV (summed over the group) are
 //     written once: no atomics, and the result does not depend on scheduling.
 // Both main kernels walk only the tiles the bottom-right causal mask leaves visible, and a
 // causal workgroup takes a heavy and a light block of one head so all cost the same.

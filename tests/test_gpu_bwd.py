@@ -100,6 +100,8 @@ SMALL = [
     (2, 2, 2, 200, 1000, 128, False),
     (1, 8, 1, 200, 300, 64, True),     # GQA group of 8, d = 64, chunk at the end
     (1, 4, 2, 64, 64, 128, True),      # one 64-row step, one key block
+    (1, 4, 2, 256, 384, 64, False),    # d = 64 non-causal, whole key blocks: no masked step
+    (2, 2, 1, 130, 200, 64, False),    # d = 64 non-causal, ragged rows and keys
 ]
 
 
