@@ -157,6 +157,14 @@ def grad_output(shape, seed) -> torch.Tensor:
     return to_bf16(_normal(rng, shape))
 
 
+def grad_output_on_device(shape, seed, device) -> torch.Tensor:
+    """dO iid N(0,1) in bf16 drawn on `device` by torch's seeded generator (the companion of
+    prefill_on_device for tensors too large to draw on the host)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+
+
 # The five workloads, by what they are.
 def single_head_fp32() -> Prefill:
     """Single head, non-causal, fp32, 128x64, scale 1/8."""

@@ -58,3 +58,25 @@ def check_o(o_gpu, o_ref, mode: str, what="O"):
     else:
         raise ValueError(mode)
     return mx, mean
+
+
+# Gradient tolerance (derived in test_gpu_bwd.py's docstring): P and dS are rounded to bf16
+# before the products, so errors scale with the root mean square of each gradient row.
+def check_grad(g, r, name, bf16_out):
+    g = to_np(g) if isinstance(g, torch.Tensor) else np.asarray(g)
+    r = np.asarray(r)
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    err = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    if rms == 0.0:
+        assert float(err.max()) == 0.0, f"{name}: reference is zero, kernel is not"
+        return 0.0, 0.0
+    rel = float(np.sqrt(np.sum(err * err)) / np.sqrt(np.sum(r * r)))
+    rms_row = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    bound = 2.0 ** -4 * (np.abs(r) + rms_row) + 2.0 ** -10 * rms + (half_ulp_bf16(r) if bf16_out else 0.0)
+    worst = float((err / bound).max())
+    print(f"  {name}: rel-l2 {rel:.2e}  max-abs {float(err.max()):.3g}  rms {rms:.3g}  worst/bound {worst:.3f}", flush=True)
+    assert rel <= 2.0 ** -6, f"{name}: relative l2 error {rel:.3g} > 2^-6"
+    assert worst <= 1.0, f"{name}: an element exceeds its bound by a factor {worst:.3g}"
+    return rel, worst
