@@ -457,7 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       issue(s + 1, qs_n, gs_n, rs_n);
       int bh, q0;
       step_rows(s, bh, q0);
-      // S = Q K^T and dP = dO V^T for the 32 rows of sub-block sb x this wave's 32 keys
+      // One sub-block at a time (a causal step whose first sub-block sees none of this
+      // wave's keys): S = Q K^T and dP = dO V^T for its 32 rows x this wave's 32 keys,
       auto scores = [&](int sb, f32x16& sc, f32x16& dp) {
         const __bf16* qsb = qs + sb * 32 * D;
         const __bf16* gsb = gs + sb * 32 * D;
@@ -471,9 +472,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           dp = mfma32x32x16(ga, vf[t], dp);
         }
       };
-      // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf),
-      // dS = P (dP - D[row]), both as bf16 MFMA operands.  Branch-free, so that it can be
-      // interleaved with independent MFMAs.
+      // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf)
+      // and dS = P (dP - D[row]) as bf16 MFMA operands,
       auto softmax = [&](int sb, const f32x16& sc, const f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
         const int qs0 = q0 + 32 * sb;
         const float* rsb = rs + sb * 64;
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                                    ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
         }
       };
-      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
+      // then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
       auto grads = [&](int sb, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
         const __bf16* qsb = qs + sb * 32 * D;
         const __bf16* gsb = gs + sb * 32 * D;
