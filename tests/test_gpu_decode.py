@@ -114,6 +114,45 @@ def test_decode_small(case):
     check_lse(lse32, L)
 
 
+def test_decode_workspace_needs_no_initialization():
+    """The workspace is scratch: one buffer, first filled with 0xA5 and later with 0xFF
+    bytes, serves calls of different shapes in turn, each checked against the oracle (no
+    result may depend on what a previous call or anything else left there)."""
+    cases = [(2, 8, 2, 1, 1000, 128, True, 0, 3), (1, 16, 2, 3, 500, 128, True, 0, 4),
+             (2, 8, 1, 1, 300, 128, True, 16, 4), (1, 4, 2, 1, 700, 64, False, 0, 7)]
+    ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device=DEV)
+    for fill in (0xA5, 0xFF):
+        ws.fill_(fill)
+        for rep in range(2):
+            for case in cases:
+                B, Hq, Hkv, T, Nk, d, causal, ps, ns = case
+                say("decode, shared workspace", hex(fill), rep, case)
+                w = workloads.decode(B, Hq, Hkv, T, Nk, d, seed=sum(case), causal=causal, page_size=ps,
+                                     num_pages=None if ps == 0 else B * (-(-Nk // ps)) + 3)
+                assert fa.fa_decode_workspace_bytes(B, Hq, Hkv, T, Nk, d, ns) <= ws.numel()
+                O, L = oracle_of(w)
+                q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+                bt = None if w.block_table is None else w.block_table.to(DEV)
+                o = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+                lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+                fa.fa_decode_splitkv(q, k, v, o, lse, causal=causal, scale=w.scale, num_splits=ns,
+                                     block_table=bt, n_k=w.n_k, workspace=ws)
+                torch.cuda.synchronize()
+                check_o(o, O, "bf16")
+                check_lse(lse, L)
+
+
+@pytest.mark.parametrize("ns", [255, 300])
+def test_decode_many_splits(ns):
+    """Hundreds of splits, each holding one 64-key piece, merged into one row per head."""
+    w = workloads.decode(1, 4, 2, 1, 64 * ns, 64, seed=4700 + ns, causal=True)
+    say("decode, many splits", ns)
+    O, L = oracle_of(w)
+    o, lse = run_decode(w, ns)
+    check_o(o, O, "bf16")
+    check_lse(lse, L)
+
+
 # ---------------------------------------------------------------------------
 # fa_lse_merge on its own
 # ---------------------------------------------------------------------------
