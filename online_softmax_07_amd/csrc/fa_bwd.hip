@@ -303,13 +303,20 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
           // P^T = 2^(s scale log2e - lse2), 0 past the mask; dS^T = P^T (dP^T - D)
           const bool need_mask = (kb0 + 32 > N_k) || (CAUSAL && kb0 + 31 > wave_row0 + shift);
           const int thr = row_lim - kb0 - 4 * hh;
+          // (a block every row of this wave sees in full takes the variant without mask tests)
           f32x16 ds;
+          auto soft = [&](auto maskc) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float p = exp2f_hw(__builtin_fmaf(s[i], scale_log2, -lse2));
-            if (need_mask && 8 * (i >> 2) + (i & 3) > thr) p = 0.f;
-            ds[i] = p * (dp[i] - Dv);
-          }
+            for (int i = 0; i < 16; ++i) {
+              float p = exp2f_hw(__builtin_fmaf(s[i], scale_log2, -lse2));
+              if constexpr (decltype(maskc)::value) {
+                if (8 * (i >> 2) + (i & 3) > thr) p = 0.f;
+              }
+              ds[i] = p * (dp[i] - Dv);
+            }
+          };
+          if (need_mask) soft(std::true_type{});
+          else soft(std::false_type{});
           bf16x8 dsf[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u)
