@@ -16,6 +16,12 @@ the forward's) and the two decode workloads (decode timed with L2
 and the Infinity Cache flushed by a 1 GiB read before every call).  ``cpu_baseline`` times
 the fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
 
+Warm-up: by default the timed workload runs back to back for 1 s before the K timed calls
+(each breakdown entry for 0.3 s): this GPU raises its clock over the first few hundred
+milliseconds of load, and a handful of warm-up calls times the ramp, not the kernel
+(B=4, H=16, N=4096 causal: 869-904 TFLOP/s after 10 calls, 979-988 after 0.6 s).
+``--warmup W`` runs exactly W untimed calls instead; the JSON reports the count made.
+
 ``--workload`` makes another workload the timed one (for profiling); ``--calib-copy``
 adds a plain 1 GiB device copy (torch's copy kernel), the reference that scales the
 HBM byte counters.
@@ -45,8 +51,10 @@ WORKLOADS = tuple(PREFILL) + ("long_prefill_8192",) + PAGED_PREFILL + BACKWARD +
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=-1,
+                   help="untimed calls before the timed ones; -1 (default): as many as fill %.1f s, "
+                        "the time this GPU takes to reach its steady clock under the load" % WARM_S)
     p.add_argument("--workload", default="prefill_d128_causal", choices=WORKLOADS)
     p.add_argument("--num-splits", type=int, default=0, help="decode split count for --workload (0 = auto)")
     p.add_argument("--no-extra", action="store_true", help="time the --workload only")
@@ -55,6 +63,10 @@ def parse():
     p.add_argument("--no-flush", action="store_true", help="decode --workload: time without the cache flush")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     return p.parse_args()
+
+
+WARM_S = 1.0          # default warm-up of the timed workload, seconds of back-to-back calls
+WARM_S_EXTRA = 0.3    # warm-up of each breakdown entry (the GPU is already at its clock)
 
 
 def main():
@@ -73,15 +85,26 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn, steps, warmup, pre=None):
-        """Per-call durations (ms) from HIP events recorded on the launch stream, and the
-        bracketed total of the K calls (pre(), e.g. a cache flush, sits outside each call's
-        bracket but inside the total)."""
-        for _ in range(warmup):
+    def warm(fn, warmup, pre=None, seconds=WARM_S):
+        """warmup >= 0: exactly that many untimed calls; < 0: calls until `seconds` of wall
+        time have passed (at least 10).  Returns the number of calls made."""
+        n = 0
+        t_end = time.perf_counter() + seconds
+        while (warmup >= 0 and n < warmup) or (warmup < 0 and (n < 10 or time.perf_counter() < t_end)):
             if pre:
                 pre()
             fn()
+            n += 1
+            if warmup < 0 and n % 16 == 0:
+                torch.cuda.synchronize()   # keep the queue short so the wall clock tracks the GPU
         torch.cuda.synchronize()
+        return n
+
+    def timed(fn, steps, warmup, pre=None, seconds=WARM_S):
+        """Per-call durations (ms) from HIP events recorded on the launch stream, the
+        bracketed total of the K calls (pre(), e.g. a cache flush, sits outside each call's
+        bracket but inside the total), and the number of warm-up calls made first."""
+        n_warm = warm(fn, warmup, pre, seconds)
         st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
@@ -96,7 +119,7 @@ def main():
             en[i].record(stream)
         t1.record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in zip(st, en)]
+        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in zip(st, en)], n_warm
 
     def make(name):
         if name in PREFILL:
@@ -194,7 +217,7 @@ def main():
     if head in DECODE:
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB: evicts L2 and MALL
         fn, nbytes, bufs = decode_case(w, args.num_splits)
-        total_ms, per = timed(fn, args.steps, args.warmup, pre=None if args.no_flush else flush_caches)
+        total_ms, per, n_warm = timed(fn, args.steps, args.warmup, pre=None if args.no_flush else flush_caches)
         avg = statistics.mean(per)
         ms_per_step = avg   # the flush between calls is not part of the step
         value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -206,7 +229,7 @@ def main():
     else:
         paged = head in PAGED_PREFILL
         fn, flops, bufs = any_prefill_case(w_inputs)
-        total_ms, per = timed(fn, args.steps, args.warmup)
+        total_ms, per, n_warm = timed(fn, args.steps, args.warmup)
         avg = statistics.mean(per)
         ms_per_step = total_ms / args.steps
         value = flops / (ms_per_step * 1e-3) / 1e12
@@ -228,7 +251,7 @@ def main():
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -253,7 +276,7 @@ def main():
                 continue
             ww = make(name)
             fn, fl, bufs = any_prefill_case(ww)
-            _, per = timed(fn, max(10, args.steps // 2), 3)
+            _, per, _ = timed(fn, max(10, args.steps // 2), -1, seconds=WARM_S_EXTRA)
             med = statistics.median(per)
             if isinstance(ww, tuple):
                 ww = ww[0]
@@ -267,7 +290,7 @@ def main():
             entry, best = {"by_num_splits": {}}, None
             for ns in list(ww.num_splits) + [0]:
                 fn, nbytes, bufs = decode_case(ww, ns)
-                _, per = timed(fn, 30, 3, pre=flush_caches)
+                _, per, _ = timed(fn, 30, -1, pre=flush_caches, seconds=WARM_S_EXTRA)
                 med = statistics.median(per)
                 gbs = nbytes / (med * 1e-3) / 1e9
                 key = "auto" if ns == 0 else str(ns)
@@ -288,7 +311,7 @@ def main():
         b = torch.empty_like(a)
         a.fill_(3)
         torch.cuda.synchronize()
-        _, per = timed(lambda: b.copy_(a), 5, 2)
+        _, per, _ = timed(lambda: b.copy_(a), 5, 2)
         result["calib_copy"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
                                 "us": round(statistics.median(per) * 1e3, 2)}
         del a, b
