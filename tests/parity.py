@@ -70,7 +70,11 @@ def check_grad(g, r, name, bf16_out):
     err = np.abs(g - r)
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     if rms == 0.0:
-        assert float(err.max()) == 0.0, f"{name}: reference is zero, kernel is not"
+        # An all-zero reference: no row sees a key, or every row that does sees exactly one
+        # (P = 1, so dS = dP - D vanishes only up to the fp32 rounding of two different dot
+        # products of length d, ~2^-20 of |dP| for unit-scale inputs).  The kernel may leave
+        # that residue, times K or Q, but nothing larger.
+        assert float(err.max()) <= 1e-4, f"{name}: reference is zero, kernel is {float(err.max()):.3g}"
         return 0.0, 0.0
     rel = float(np.sqrt(np.sum(err * err)) / np.sqrt(np.sum(r * r)))
     rms_row = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
