@@ -1,5 +1,6 @@
 /*
- * fa.h -- FlashAttention forward pass and split-KV decode for AMD Instinct MI355X (gfx950).
+ * fa.h -- FlashAttention forward and backward passes and split-KV decode for AMD Instinct
+ * MI355X (gfx950).
  *
  * C linkage; no C++ or framework types cross this boundary.  Every tensor argument is a
  * DEVICE pointer owned by the caller.  The library never allocates, frees or synchronises:
@@ -51,7 +52,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
-  FA_ERR_BAD_SHAPE = 2,    /* a size is <= 0, H_q % H_kv != 0, scale not > 0, bad split/page args */
+  FA_ERR_BAD_SHAPE = 2,    /* B, H or d <= 0, a length < 0, H_q % H_kv != 0, scale not > 0, bad split/page args */
   FA_ERR_UNSUPPORTED = 3,  /* head dimension or dtype the library has no kernel for */
   FA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than fa_decode_workspace_bytes() */
   FA_ERR_ALIGNMENT = 5,    /* a tensor pointer is not 16-byte aligned */
