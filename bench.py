@@ -290,7 +290,7 @@ def main():
             entry, best = {"by_num_splits": {}}, None
             for ns in list(ww.num_splits) + [0]:
                 fn, nbytes, bufs = decode_case(ww, ns)
-                _, per, _ = timed(fn, 30, -1, pre=flush_caches, seconds=WARM_S_EXTRA)
+                _, per, _ = timed(fn, 100, -1, pre=flush_caches, seconds=WARM_S_EXTRA)
                 med = statistics.median(per)
                 gbs = nbytes / (med * 1e-3) / 1e9
                 key = "auto" if ns == 0 else str(ns)
