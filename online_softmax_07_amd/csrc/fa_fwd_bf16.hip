@@ -26,10 +26,10 @@
 //     (plain for K, transposing for V) bank-conflict free.
 //   * Independent accumulators are interleaved; K fragments are read two k-steps ahead of
 //     the score MFMAs that consume them, V fragments one step ahead.
-//   * The running max is only moved (and l, O rescaled) when a row's tile max exceeds it
-//     by more than 2^8 in the exponent; until then p <= 2^8.  O = acc / l and
-//     LSE = m + ln l are exact for any reference m, so this only skips work (the skip is
-//     wave-uniform).  O is divided by the sum of the same bf16-rounded P the PV product
+//   * The reference max m is only moved (and l, O rescaled) when the weights computed
+//     against it would sum above 2^30 on some lane of the wave (or no reference exists yet);
+//     the row max itself is then computed, otherwise never.  O = acc / l and LSE = m + ln l
+//     are exact for any reference m, so this only skips work (the test is wave-uniform).  O is divided by the sum of the same bf16-rounded P the PV product
 //     uses (v_dot2 against (1, 1)), so the rounding of a dominant weight (which need not
 //     be 1 under a lagging max) cancels in O = sum p V / sum p; the LSE uses the fp32 sum.
 //   * The wave raises its issue priority for its MFMA sections (s_setprio), so the two
@@ -48,7 +48,10 @@ namespace fa {
 // per SIMD on each CU (one 8-wave workgroup at d = 128, two 4-wave ones at d = 64): every
 // K/V tile staged in LDS serves 256 rows, and at d = 128 the LDS a second workgroup would
 // take holds 128-key tiles instead.
-constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag behind
+// A lane's tile sum of weights, 2^(s scale log2e - m) over its keys of one row, above which
+// the reference m is moved to the tile max: the weights then stay below 2^30, far inside
+// fp32 and bf16 range, and the fp32 sums keep their relative precision.
+constexpr float kRescaleSum = 1073741824.0f;
 
 template <int D, int BC, int NW, int RH>
 struct FwdTile {
@@ -324,39 +327,50 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
           }
 
           // ---- online softmax (base 2, lazily rescaled) ----
-          float mx = kNegInf;
+          // Exponentiate against the running reference m as it stands; only when a lane's
+          // tile sum comes out above kRescaleSum (or no reference exists yet) is the tile max
+          // taken, the carries rescaled to it and the exponentials redone.  Any reference
+          // gives the same O and LSE; this one only moves when the weights would grow large.
+          auto exps = [&](float m_use) {
+            float sum = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
+            for (int u = 0; u < BC / 16; ++u) {
+              const f32x16& sk = s[x][u >> 1];
+              const int r0 = (u & 1) * 8;
+              f32x8 e;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[x][kb][r]);
-          mx = max_halves(mx) * scale_log2;
-          if (wave_any(mx > m_run[x] + kRescaleSlack)) {
-            const float m_new = fmaxf(m_run[x], mx);
-            // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
-            const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run[x] - m_new);
-            l_run[x] *= alpha;
-            lb_run[x] *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < T::NCB; ++cb) o[x][cb] *= alpha;
-            m_run[x] = m_new;
-          }
-          const float m_use = m_run[x] == kNegInf ? 0.f : m_run[x];  // a row with no key yet: all p = 0
-#pragma unroll
-          for (int kb = 0; kb < T::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              s[x][kb][r] = exp2f_hw(__builtin_fmaf(s[x][kb][r], scale_log2, -m_use));
-              l_run[x] += s[x][kb][r];
+              for (int r = 0; r < 8; ++r) {
+                e[r] = exp2f_hw(__builtin_fmaf(sk[r0 + r], scale_log2, -m_use));
+                sum += e[r];
+              }
+              pf[x][u] = to_bf16x8(e);  // P^T operands (bf16, RNE) of the BC/16 key steps
             }
-          // P^T operands (bf16, RNE) for the BC/16 key steps; lb sums exactly these values
+            return sum;
+          };
+          float tsum = m_run[x] == kNegInf ? 0.f : exps(m_run[x]);
+          if (wave_any(m_run[x] == kNegInf || !(tsum <= kRescaleSum))) {
+            float mx = kNegInf;
 #pragma unroll
-          for (int u = 0; u < BC / 16; ++u) {
-            const f32x16& sk = s[x][u >> 1];
-            const int r0 = (u & 1) * 8;
-            pf[x][u] = to_bf16x8(f32x8{sk[r0 + 0], sk[r0 + 1], sk[r0 + 2], sk[r0 + 3],
-                                       sk[r0 + 4], sk[r0 + 5], sk[r0 + 6], sk[r0 + 7]});
-            lb_run[x] = sum_bf16x8(pf[x][u], lb_run[x]);
+            for (int kb = 0; kb < T::NKB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[x][kb][r]);
+            mx = max_halves(mx) * scale_log2;
+            const float m_new = fmaxf(m_run[x], mx);
+            if (m_new != m_run[x]) {
+              // 0 when m_run = -inf; 1 for a row that still has no key (both -inf)
+              const float alpha = m_new == kNegInf ? 1.f : exp2f_hw(m_run[x] - m_new);
+              l_run[x] *= alpha;
+              lb_run[x] *= alpha;
+#pragma unroll
+              for (int cb = 0; cb < T::NCB; ++cb) o[x][cb] *= alpha;
+              m_run[x] = m_new;
+            }
+            tsum = exps(m_run[x] == kNegInf ? 0.f : m_run[x]);  // a row with no key yet: all p = 0
           }
+          l_run[x] += tsum;
+          // lb sums exactly the bf16 weights the PV product uses
+#pragma unroll
+          for (int u = 0; u < BC / 16; ++u) lb_run[x] = sum_bf16x8(pf[x][u], lb_run[x]);
         }
 
         // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
