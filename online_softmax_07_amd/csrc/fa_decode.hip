@@ -24,7 +24,10 @@
 // (valid) address and masked: their P is exactly 0, so no zero fill is needed.  With a
 // block table, every lane fetches the page of one key two chunks ahead and the row
 // addresses are exchanged with ds_bpermute, so the dependent table load never stalls the
-// stream.  At the end the four waves' carries are merged in LDS by the LSE rule.
+// stream.  K and V are read exactly once per call, so their loads are nontemporal: the
+// lines stream through the caches without displacing anything (on this chip that raises a
+// streaming read from about 5.8 to 6.7 TB/s).  At the end the four waves' carries are
+// merged in LDS by the LSE rule.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -115,14 +118,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       const int r = __builtin_amdgcn_ds_bpermute(4 * (kb * 16 + l16), rows);
       const __bf16* kr = K + (size_t)r * D + 8 * g4;
 #pragma unroll
-      for (int t = 0; t < C::KT; ++t) c.k[kb][t] = *reinterpret_cast<const bf16x8*>(kr + 32 * t);
+      for (int t = 0; t < C::KT; ++t)
+        c.k[kb][t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * t)));
     }
     // V: load i covers VROWS_PER_LOAD whole rows, 16 bytes per lane
 #pragma unroll
     for (int i = 0; i < C::VL; ++i) {
       const int row = i * C::VROWS_PER_LOAD + lane / (D / 8);
       const int r = __builtin_amdgcn_ds_bpermute(4 * row, rows);
-      c.v[i] = *reinterpret_cast<const u32x4*>(V + (size_t)r * D + (lane % (D / 8)) * 8);
+      c.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + (size_t)r * D + (lane % (D / 8)) * 8));
     }
   };
 
