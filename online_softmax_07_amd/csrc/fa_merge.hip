@@ -43,14 +43,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     }
   }
 
-  // m* and sum_s e^{lse_s - m*} over all splits (each lane holds every 64th lse)
-  float mx = kNegInf;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, LSE_part[(size_t)s * rows + row]);
+  // m* and sum_s e^{lse_s - m*} over all splits (each lane holds every 64th lse; the first
+  // one stays in a register, so up to 64 splits need a single load per lane)
+  const float ls0 = lane < ns ? LSE_part[(size_t)lane * rows + row] : kNegInf;
+  float mx = ls0;
+  for (int s = lane + 64; s < ns; s += 64) mx = fmaxf(mx, LSE_part[(size_t)s * rows + row]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, off));
   float sum = 0.f;
-  if (mx != kNegInf)
-    for (int s = lane; s < ns; s += 64) sum += exp2f_hw((LSE_part[(size_t)s * rows + row] - mx) * kLog2e);
+  if (mx != kNegInf) {
+    sum = exp2f_hw((ls0 - mx) * kLog2e);
+    for (int s = lane + 64; s < ns; s += 64) sum += exp2f_hw((LSE_part[(size_t)s * rows + row] - mx) * kLog2e);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += shfl_xor_f(sum, off);
   const float lse = mx == kNegInf ? kNegInf : mx + log2f_hw(sum) * kLn2;
@@ -65,14 +69,27 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
 #pragma unroll
       for (int i = 0; i < kMergeMaxPerLane; ++i) acc[i] = __builtin_fmaf(w, v[u][i], acc[i]);
     }
-    // further batches (more than kMergeWaves * kMergeBatch splits)
-    for (int s = wave + kMergeWaves * kMergeBatch; s < ns; s += kMergeWaves) {
-      const float w = exp2f_hw((LSE_part[(size_t)s * rows + row] - lse) * kLog2e);
-      const float* Op = O_part + ((size_t)s * rows + row) * d;
+    // further batches (more than kMergeWaves * kMergeBatch splits), each again issued as
+    // one round of loads before its weights are applied
+    for (int s0 = wave + kMergeWaves * kMergeBatch; s0 < ns; s0 += kMergeWaves * kMergeBatch) {
 #pragma unroll
-      for (int i = 0; i < kMergeMaxPerLane; ++i) {
-        const int c = lane + 64 * i;
-        if (c < d) acc[i] = __builtin_fmaf(w, Op[c], acc[i]);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = s0 + kMergeWaves * u;
+        const bool ok = s < ns;
+        const int sc = ok ? s : 0;
+        ls[u] = ok ? LSE_part[(size_t)sc * rows + row] : kNegInf;
+        const float* Op = O_part + ((size_t)sc * rows + row) * d;
+#pragma unroll
+        for (int i = 0; i < kMergeMaxPerLane; ++i) {
+          const int c = lane + 64 * i;
+          v[u][i] = (ok && i < nper && c < d) ? Op[c] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = exp2f_hw((ls[u] - lse) * kLog2e);
+#pragma unroll
+        for (int i = 0; i < kMergeMaxPerLane; ++i) acc[i] = __builtin_fmaf(w, v[u][i], acc[i]);
       }
     }
   }
