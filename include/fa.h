@@ -147,7 +147,9 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * num_splits == 0.  Splitting pays when batch x KV heads is far below the number of
  * compute units; the aim is about one full wave of workgroups and no mostly idle second
  * wave (page "Attention kernel chains", chain "How many splits for decode"), here for the
- * MI355X's 256 compute units.  Returns >= 1, or 0 on invalid sizes.
+ * MI355X's 256 compute units: one workgroup per CU, or two per CU (both resident at once)
+ * when one per CU would leave splits shorter than 4096 keys.  Never more splits than
+ * 256-key pieces of the cache.  Returns >= 1, or 0 on invalid sizes.
  */
 int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d);
 

@@ -8,8 +8,8 @@
 
 namespace {
 
-constexpr int kNumCU = 256;        // MI355X compute units
-constexpr int kDecodeWGPerCU = 1;  // one split workgroup per CU: more splits only grow the merge
+constexpr int kNumCU = 256;             // MI355X compute units
+constexpr int kDecodeLongSplit = 4096;  // keys: a split at least this long streams well alone on a CU
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -38,9 +38,15 @@ int split_len_of(int n_k, int ns) {
 int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
   const long long row_chunks = ((long long)(H_q / H_kv) * T + 15) / 16;
   const long long base = (long long)B * H_kv * row_chunks;  // workgroups without splitting
-  const long long target = (long long)kNumCU * kDecodeWGPerCU;
+  // One split workgroup per CU when that leaves long splits; shorter splits go two to a CU
+  // (the decode kernel fits twice), so one workgroup's start (Q and block-table loads) and
+  // end (carry merge, partial write) overlap the other's stream.  More splits than that
+  // only add partials to merge.
+  const long long target = kNumCU;
   if (base < 1) return 1;  // no query row
-  long long ns = base >= target ? 1 : target / base;
+  if (base >= target) return 1;
+  long long ns = target / base;
+  if ((long long)N_k < ns * kDecodeLongSplit) ns = 2 * target / base;
   const long long max_useful = ((long long)N_k + 4 * fa::kDecodeChunk - 1) / (4 * fa::kDecodeChunk);
   if (ns > max_useful) ns = max_useful;  // at least one chunk per wave
   if (ns < 1) ns = 1;

@@ -207,9 +207,10 @@ def test_workspace_and_split_sizes():
     assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == 4 * 512 * 128 * 4 + 4 * 512 * 4
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 8 * 32 * 128 * 4 + 1024  # empty cache, 8 splits
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, -1, 128, 8) == 0                      # invalid length
-    # the automatic split count aims at one wave of one workgroup on each of 256 CUs
+    # the automatic split count aims at one wave of one workgroup on each of 256 CUs, two when
+    # the splits would be short
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 131072, 128) == 32
-    assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 4
+    assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 8   # 2048-key splits: two workgroups per CU
     assert fa.fa_decode_num_splits(256, 32, 8, 1, 4096, 128) == 1
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 300, 128) == 2  # never more splits than 256-key pieces
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 0) == fa.fa_decode_workspace_bytes(
