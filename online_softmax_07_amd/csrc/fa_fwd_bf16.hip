@@ -411,12 +411,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     }
 
     // ---- epilogue: one division, O and LSE written once ----
-    if constexpr (D == 128 && BC == 128 && RH == 1 && sizeof(OutT) == 2 && !CAUSAL) {
+    if constexpr (D == 128 && BC == 128 && RH == 1 && sizeof(OutT) == 2) {
       // bf16 rows go out through LDS so each store writes whole rows (four 256-byte rows
-      // per instruction) instead of 8 bytes of 32 rows: +2 % on the full mask.  (Measured
-      // 1-2 % slower under the causal mask, whose workgroups run a second block after this
-      // one, so that path keeps the direct stores.)  The wave's 32 x 128 block uses 8 KB of
-      // stage 1, which no wave reads again before the last barrier of the tile loop.
+      // per instruction) instead of 8 bytes of 32 rows (+2-3 %).  The wave's 32 x 128 block
+      // uses 8 KB of stage 1: every wave has finished reading it (the tile loop's last
+      // barrier), and the next causal block refills it only after its first barrier.
       __bf16* ost = (wave < 4 ? Ks1 : Vs1) + (wave & 3) * (32 * D);
       // the lane-dependent offsets below are made here, not hoisted out of the pass loop
       // (kept live across the main loop they would crowd its registers)
