@@ -411,42 +411,55 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
     }
 
     // ---- epilogue: one division, O and LSE written once ----
-    if constexpr (D == 128 && BC == 128 && RH == 1 && sizeof(OutT) == 2) {
-      // bf16 rows go out through LDS so each store writes whole rows (four 256-byte rows
-      // per instruction) instead of 8 bytes of 32 rows (+2-3 %).  The wave's 32 x 128 block
-      // uses 8 KB of stage 1: every wave has finished reading it (the tile loop's last
-      // barrier), and the next causal block refills it only after its first barrier.
-      __bf16* ost = (wave < 4 ? Ks1 : Vs1) + (wave & 3) * (32 * D);
+    if constexpr (sizeof(OutT) == 2 && !PAGED && NW * 32 * D <= 2 * T::STAGE) {
+      // bf16 rows go out through LDS so each store writes whole rows (1 KB of consecutive
+      // rows per instruction) instead of 8 bytes of 32 rows (+2-3 % at d = 128).  Each
+      // 32-row half of the wave's block (32 x D) takes 64*D bytes of stage 1: every wave has
+      // finished reading it (the tile loop's last barrier), and the next causal block
+      // refills it only after its first barrier.
+      constexpr int CH = D / 8;                   // 16-byte chunks per row
+      constexpr int RPI = 64 / CH;                // rows per wave-wide 16-byte access
+      constexpr int WPS = T::STAGE / (32 * D);    // waves per stage array
+      __bf16* ost = (wave < WPS ? Ks1 : Vs1) + (wave % WPS) * (32 * D);
       // the lane-dependent offsets below are made here, not hoisted out of the pass loop
       // (kept live across the main loop they would crowd its registers)
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int r32 = ln & 31, hh2 = ln >> 5;
-      const float l_tot = l_run[0] + shfl_xor_f(l_run[0], 32);
-      const float lb_tot = lb_run[0] + shfl_xor_f(lb_run[0], 32);
-      const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
 #pragma unroll
-      for (int cb = 0; cb < T::NCB; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = {o[0][cb][4 * g] * inv, o[0][cb][4 * g + 1] * inv, o[0][cb][4 * g + 2] * inv,
-                           o[0][cb][4 * g + 3] * inv};
-          // 16-byte chunk cb*4+g of row r32, XOR-swizzled by the row so the 32 rows spread over the banks
-          *reinterpret_cast<bf16x4*>(ost + r32 * D + (((cb * 4 + g) ^ (r32 & 15)) << 3) + 4 * hh2) =
-              __builtin_convertvector(v, bf16x4);
+      for (int x = 0; x < RH; ++x) {
+        const float l_tot = l_run[x] + shfl_xor_f(l_run[x], 32);
+        const float lb_tot = lb_run[x] + shfl_xor_f(lb_run[x], 32);
+        const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+        if (x > 0) {  // the previous half has been read back
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 4 * i + (ln >> 4), ch = ln & 15;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(ost + row * D + ((ch ^ (row & 15)) << 3));
-        if (wave_row0 + row < N_q)
-          *reinterpret_cast<u32x4*>(O + ((size_t)bh * N_q + wave_row0 + row) * D + ch * 8) = val;
+        for (int cb = 0; cb < T::NCB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {o[x][cb][4 * g] * inv, o[x][cb][4 * g + 1] * inv, o[x][cb][4 * g + 2] * inv,
+                             o[x][cb][4 * g + 3] * inv};
+            // chunk cb*4+g of row r32, XOR-swizzled by the row so the 32 rows spread over the banks
+            *reinterpret_cast<bf16x4*>(ost + r32 * D + (((cb * 4 + g) ^ (r32 & (CH - 1))) << 3) + 4 * hh2) =
+                __builtin_convertvector(v, bf16x4);
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row0 = wave_row0 + 32 * x;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int row = RPI * i + ln / CH, ch = ln % CH;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ost + row * D + ((ch ^ (row & (CH - 1))) << 3));
+          if (row0 + row < N_q)
+            *reinterpret_cast<u32x4*>(O + ((size_t)bh * N_q + row0 + row) * D + ch * 8) = val;
+        }
+        if (LSE != nullptr && hh == 0 && qrow[x] < N_q)
+          LSE[(size_t)bh * N_q + qrow[x]] = l_tot > 0.f ? (m_run[x] + log2f_hw(l_tot)) * kLn2 : kNegInf;
       }
-      if (LSE != nullptr && hh == 0 && qrow[0] < N_q)
-        LSE[(size_t)bh * N_q + qrow[0]] = l_tot > 0.f ? (m_run[0] + log2f_hw(l_tot)) * kLn2 : kNegInf;
       continue;
     }
 #pragma unroll
