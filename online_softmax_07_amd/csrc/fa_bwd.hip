@@ -132,6 +132,40 @@ __device__ __forceinline__ void store_row(OutT* row, const f32x16 (&acc)[D / 32]
     }
 }
 
+// The same block in bf16 through a wave-private 32 x D LDS area, so each store writes whole
+// rows (1 KB of consecutive rows per instruction) instead of 8 bytes of 32 rows.  `dst` is
+// the block's first row; rows from n_valid on are not written.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(__bf16* dst, int n_valid, __bf16* area,
+                                               const f32x16 (&acc)[D / 32], float mul, int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH;  // 16-byte chunks per row, rows per access
+  int ln = lane;
+  asm volatile("" : "+v"(ln));  // offsets made here, not hoisted into the main loop
+  const int r32 = ln & 31, hh = ln >> 5;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // an earlier block is read back
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = {acc[cb][4 * g] * mul, acc[cb][4 * g + 1] * mul, acc[cb][4 * g + 2] * mul,
+                       acc[cb][4 * g + 3] * mul};
+      // chunk cb*4+g of row r32, XOR-swizzled by the row so the 32 rows spread over the banks
+      *reinterpret_cast<bf16x4*>(area + r32 * D + (((cb * 4 + g) ^ (r32 & (CH - 1))) << 3) + 4 * hh) =
+          __builtin_convertvector(v, bf16x4);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + ln / CH, ch = ln % CH;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(area + row * D + ((ch ^ (row & (CH - 1))) << 3));
+    if (row < n_valid) *reinterpret_cast<u32x4*>(dst + (size_t)row * D + ch * 8) = val;
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -634,7 +668,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       step(s, Qs0, Gs0, Rs0, Qs1, Gs1, Rs1);
       if (s + 1 < n_steps) step(s + 1, Qs1, Gs1, Rs1, Qs0, Gs0, Rs0);
     }
-    if (key < N_k) {
+    if constexpr (sizeof(OutT) == 2 && 4 * 32 * D <= 2 * STAGE) {
+      // bf16 out: through stage 1, which every wave has finished reading (the last step's
+      // barrier) and the next causal block refills only after its first barrier
+      __bf16* area = (wave < 2 ? Qs1 : Gs1) + (wave & 1) * (32 * D);
+      const size_t row0 = (((size_t)b * H_kv + hk) * N_k + kw0) * D;
+      store_rows_lds<D>(reinterpret_cast<__bf16*>(dK) + row0, N_k - kw0, area, dk, scale, lane);
+      store_rows_lds<D>(reinterpret_cast<__bf16*>(dV) + row0, N_k - kw0, area, dv, 1.f, lane);
+    } else if (key < N_k) {
       const size_t row = (((size_t)b * H_kv + hk) * N_k + key) * D;
       store_row<D>(dK + row, dk, scale, hh);
       store_row<D>(dV + row, dv, 1.f, hh);
