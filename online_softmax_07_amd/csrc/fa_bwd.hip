@@ -376,7 +376,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       tile_step(j, Ks0, Vs0, Ks1, Vs1);
       if (j + 1 < n_tiles) tile_step(j + 1, Ks1, Vs1, Ks0, Vs0);
     }
-    if (qrow < N_q) store_row<D>(dQ + ((size_t)bh * N_q + qrow) * D, dq, scale, hh);
+    if constexpr (sizeof(OutT) == 2 && NW * 32 * D <= 2 * STAGE) {
+      // bf16 out: through stage 1, which every wave has finished reading (the last tile's
+      // barrier) and the next causal block refills only after its first barrier
+      __bf16* area = (wave < NW / 2 ? Ks1 : Vs1) + (wave % (NW / 2)) * (32 * D);
+      store_rows_lds<D>(reinterpret_cast<__bf16*>(dQ) + ((size_t)bh * N_q + wave_row0) * D, N_q - wave_row0, area,
+                        dq, scale, lane);
+    } else if (qrow < N_q) {
+      store_row<D>(dQ + ((size_t)bh * N_q + qrow) * D, dq, scale, hh);
+    }
   }
 }
 
