@@ -3,24 +3,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu]
 
-Default step: one fa_fwd call on the prefill workload B=4, H_q=H_kv=16, N=4096, d=128,
-causal (bottom-right), bf16 in, bf16 O and fp32 LSE out, inputs resident in HBM.  The
-headline ``value`` is its attention throughput in TFLOP/s (4 N^2 d per head, halved for
-causal).  ``roofline`` prices the dominant kernel's average launch (HIP events recorded on
-the stream the library launches on) against the dense bf16 MFMA peak (prefill) or the
-HBM peak (decode), with ``traffic`` taken from the committed rocprofv3 counter summary
-when it was measured on the current kernel source.  ``breakdown`` adds the other
-prefill variants, the long causal prefill, the chunked prefill over a paged cache (FLOPs:
-4 d per visible query-key pair, exact), the backward pass at the prefill shape (FLOPs: 2.5x
-the forward's) and the two decode workloads (decode timed with L2
-and the Infinity Cache flushed by a 1 GiB read before every call).  ``cpu_baseline`` times
-the fp64 oracle on a bounded sample of the headline workload.  Prints exactly one JSON line.
+Default step: one fa_fwd call on the long causal prefill B=1, H_q=H_kv=32, N=8192, d=128
+(1% of key rows scaled x8), bf16 in, bf16 O and fp32 LSE out, inputs resident in HBM: the
+largest of the prefill configurations that fit one GPU.  The headline ``value`` is its
+attention throughput in TFLOP/s (4 N^2 d per head, halved for causal) over the bracketed K
+timed calls.  ``roofline`` prices the dominant kernel's average launch (HIP events
+recorded on the stream the library launches on) against the dense bf16 MFMA peak
+(prefill) or the HBM peak (decode), with ``traffic`` taken from the committed rocprofv3
+counter summary when it was measured on the current kernel source.  ``gpu_clock_mhz`` is
+the shader clock measured by one wave right before and right after the timed region;
+``calib`` the ceilings of the committed calibration kernels (an MFMA-only loop and a
+one-pass streaming read) measured after everything else; ``host`` the CPU model.
+``breakdown`` adds the other prefill variants (including B=4, H=16, N=4096 at d=128 and
+d=64), the chunked prefill over a paged cache (FLOPs: 4 d per visible query-key pair,
+exact), the backward pass at the B=4 prefill shape (FLOPs: 2.5x the forward's) and the two
+decode workloads (decode timed with L2 and the Infinity Cache flushed by a 1 GiB read
+before every call).  ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+headline workload.  Prints exactly one JSON line.
 
 Warm-up: by default the timed workload runs back to back for 1 s before the K timed calls
 (each breakdown entry for 0.3 s): this GPU raises its clock over the first few hundred
-milliseconds of load, and a handful of warm-up calls times the ramp, not the kernel
-(B=4, H=16, N=4096 causal: 869-904 TFLOP/s after 10 calls, 979-988 after 0.6 s).
-``--warmup W`` runs exactly W untimed calls instead; the JSON reports the count made.
+milliseconds of load, and a handful of warm-up calls times the ramp as well as the kernel.
+``--warmup W`` runs exactly W untimed calls instead; the JSON reports the count made and
+the clock.
 
 ``--workload`` makes another workload the timed one (for profiling); ``--calib-copy``
 adds a plain 1 GiB device copy (torch's copy kernel), the reference that scales the
@@ -55,12 +60,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=-1,
                    help="untimed calls before the timed ones; -1 (default): as many as fill %.1f s, "
                         "the time this GPU takes to reach its steady clock under the load" % WARM_S)
-    p.add_argument("--workload", default="prefill_d128_causal", choices=WORKLOADS)
+    p.add_argument("--workload", default="long_prefill_8192", choices=WORKLOADS)
     p.add_argument("--num-splits", type=int, default=0, help="decode split count for --workload (0 = auto)")
     p.add_argument("--no-extra", action="store_true", help="time the --workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy (counter calibration)")
     p.add_argument("--no-flush", action="store_true", help="decode --workload: time without the cache flush")
+    p.add_argument("--no-calib", action="store_true", help="skip the calibration ceilings")
     p.add_argument("--out", default=None, help="also write the JSON line to this file")
     return p.parse_args()
 
@@ -79,7 +85,7 @@ def main():
 
     import torch
     sys.path.insert(0, HERE)
-    from online_softmax_07_amd import build as fabuild, fa, roofline as rl, workloads
+    from online_softmax_07_amd import build as fabuild, calib, fa, roofline as rl, workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -100,16 +106,20 @@ def main():
         torch.cuda.synchronize()
         return n
 
-    def timed(fn, steps, warmup, pre=None, seconds=WARM_S):
+    def timed(fn, steps, warmup, pre=None, seconds=WARM_S, clocks=None):
         """Per-call durations (ms) from HIP events recorded on the launch stream, the
         bracketed total of the K calls (pre(), e.g. a cache flush, sits outside each call's
-        bracket but inside the total), and the number of warm-up calls made first."""
+        bracket but inside the total), and the number of warm-up calls made first.  With
+        `clocks` (a dict), the shader clock is measured right before and right after the
+        bracket, outside it."""
         n_warm = warm(fn, warmup, pre, seconds)
         st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        if clocks is not None:
+            clocks["before_timed"] = round(calib.shader_clock_mhz(dev, stream), 0)
         t0.record(stream)
         for i in range(steps):
             if pre:
@@ -119,6 +129,8 @@ def main():
             en[i].record(stream)
         t1.record(stream)
         torch.cuda.synchronize()
+        if clocks is not None:
+            clocks["after_timed"] = round(calib.shader_clock_mhz(dev, stream), 0)
         return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in zip(st, en)], n_warm
 
     def make(name):
@@ -214,10 +226,12 @@ def main():
         w = w[0]
     s = w.shape
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
+    clocks = {}
     if head in DECODE:
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB: evicts L2 and MALL
         fn, nbytes, bufs = decode_case(w, args.num_splits)
-        total_ms, per, n_warm = timed(fn, args.steps, args.warmup, pre=None if args.no_flush else flush_caches)
+        total_ms, per, n_warm = timed(fn, args.steps, args.warmup, pre=None if args.no_flush else flush_caches,
+                                      clocks=clocks)
         avg = statistics.mean(per)
         ms_per_step = avg   # the flush between calls is not part of the step
         value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -229,7 +243,7 @@ def main():
     else:
         paged = head in PAGED_PREFILL
         fn, flops, bufs = any_prefill_case(w_inputs)
-        total_ms, per, n_warm = timed(fn, args.steps, args.warmup)
+        total_ms, per, n_warm = timed(fn, args.steps, args.warmup, clocks=clocks)
         avg = statistics.mean(per)
         ms_per_step = total_ms / args.steps
         value = flops / (ms_per_step * 1e-3) / 1e12
@@ -262,6 +276,8 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel,
                      "avg_launch_us": round(avg * 1e3, 2)},
+        "gpu_clock_mhz": clocks,
+        "host": host_info(),
     }
     traffic = load_traffic(w.name, fabuild)
     if traffic is not None:
@@ -316,6 +332,19 @@ def main():
                                 "us": round(statistics.median(per) * 1e3, 2)}
         del a, b
 
+    # ---- calibrated ceilings (context for the fractions of the published peaks) ----
+    if not args.no_calib:
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        mf = calib.mfma_ceiling(dev, stream)
+        sr = calib.stream_read_ceiling(dev, stream, flush=flush_caches)
+        del flush
+        result["calib"] = {
+            "mfma_loop": {**mf, "frac_of_peak": round(mf["tflops"] / rl.PEAK_BF16_MFMA_TFLOPS, 4)},
+            "stream_read": {**sr, "frac_of_peak": round(sr["GB/s"] / rl.PEAK_HBM_GBPS, 4)},
+        }
+        ceiling = mf["tflops"] if unit == "TFLOP/s" else sr["GB/s"]
+        result["roofline"]["frac_of_calibrated"] = round(achieved / ceiling, 4)
+
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the timed workload ----
     if not args.no_cpu and head not in DECODE and head not in BACKWARD:
         result["cpu_baseline"] = cpu_baseline(w, rl)
@@ -325,6 +354,20 @@ def main():
     if args.out:
         with open(args.out, "w") as f:
             f.write(line + "\n")
+
+
+def host_info():
+    """CPU model and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(w, rl):

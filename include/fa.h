@@ -28,7 +28,7 @@
  *   O[b,h,i,:] = sum_j p_j V[b,h_kv,j,:],  p = softmax of the visible x
  *           (page "Kernel visualization: Flash Attention 1", "Derivation")
  *   LSE[b,h,i] = ln sum_j e^{x_j}  over visible j  (natural log of the scaled scores; chain
- *           "What the backward pass saves": one fp32 log-sum-exp per query row)
+ *           "What the backward pass saves": the forward keeps this one fp32 value per row)
  *   A row with no visible key (causal with N_q > N_k, or N_k = 0) gets O = 0 and LSE = -inf.
  *
  * Sizes: B, H_q, H_kv and d are >= 1; the sequence lengths (N_q, N_k, T, rows) may be 0.
@@ -120,7 +120,7 @@ size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q);
  * fa_bwd -- gradients of the forward pass: dQ, dK, dV for the upstream gradient dO.
  *
  * Defined by: page "Attention kernel chains", chain "What the backward pass saves": the
- * forward keeps Q, K, V, O and one fp32 LSE per query row (fa_fwd's LSE output), each
+ * forward keeps its inputs, its output O and the fp32 LSE of every row (fa_fwd's LSE output), each
  * probability tile is rebuilt on chip as P = exp(S - LSE), and one extra row vector
  * D = rowsum(dO * O) is computed before the main loops.  The rest is the chain rule of
  * the forward definition: dP = dO V^T, dS = P * (dP - D), dV = P^T dO, dK = scale dS^T Q,
@@ -167,7 +167,8 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  *
  * Defined by: page "Attention kernel chains", chains "How many splits for decode" (the key
  * axis is cut into num_splits contiguous chunks, one worker each), "The log-sum-exp merge"
- * (each worker writes a normalized partial output and its lse; any split is exact), "GQA
+ * (every split stores its own output, already divided by its own sum, plus the log of that
+ * sum; the merge recovers the exact result for any split), "GQA
  * loads KV once per group" (the H_q/H_kv query heads of a group are stacked as the rows of
  * one tile so each KV tile is read once per group) and "The block-table cost of paged
  * attention" (one int32 page index per page_size-token block).
@@ -181,7 +182,8 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  *     an entry outside the pool is undefined behaviour, as in any gather.
  *   causal: 0 (every cached key visible) or 1 (bottom-right: query t sees j <= N_k - T + t).
  *   num_splits: >= 1, or 0 for fa_decode_num_splits().  Splits are contiguous key ranges of
- *     equal length rounded up to 64 keys; trailing splits may be empty.
+ *     equal length rounded up to 64 keys; trailing splits may be empty.  num_splits * B*H_q*T
+ *     must stay below 2^31 (FA_ERR_BAD_SHAPE otherwise; fa_decode_workspace_bytes returns 0).
  *   workspace: >= fa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
  *     that is 0).  d == 128 or 64.
  */

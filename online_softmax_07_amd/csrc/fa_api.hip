@@ -147,6 +147,7 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
   const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * H_q * T;
+  if ((long long)ns * (long long)rows > 0x7fffffffLL) return 0;  // partial index past 32 bits: rejected
   return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float));
 }
 
@@ -170,6 +171,8 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
       (block_table && !aligned4(block_table)))
     return FA_ERR_ALIGNMENT;
   const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
+  // every partial row index (split * rows + row) must fit 32 bits, as in fa_lse_merge
+  if (ns > 1 && (long long)ns * B * H_q * T > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
   const size_t need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGNMENT;

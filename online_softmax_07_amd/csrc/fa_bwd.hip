@@ -1,7 +1,7 @@
 // FlashAttention backward, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
 //
 // What is kept from the forward pass and how P comes back (page "Attention kernel chains",
-// chain "What the backward pass saves"): Q, K, V, O and one fp32 log-sum-exp per query row;
+// chain "What the backward pass saves"): the inputs, the output and a single fp32 LSE value for each query row;
 // each probability tile is rebuilt on chip as P = exp(S - LSE), and the softmax gradient
 // uses one extra row vector D = rowsum(dO * O), computed once before the main loops.  With
 // dS = P * (dP - D), dP = dO V^T, the gradients are dV = P^T dO, dK = scale dS^T Q and

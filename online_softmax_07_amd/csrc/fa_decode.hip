@@ -11,7 +11,8 @@
 //     is slot j % page_size of pool page block_table[b][j / page_size];
 //   * "The causal mask for a decode step": query t of the T new ones sits at position
 //     N_k - T + t and sees keys j <= N_k - T + t;
-//   * "The log-sum-exp merge": each split writes its normalized partial output and lse.
+//   * "The log-sum-exp merge": a split stores its output divided by its own sum, and the
+//     log of that sum, for the merge to weigh.
 //
 // Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk goes
 // to blockIdx.z).  Decode is a bytes problem, so the kernel is built around keeping loads
@@ -89,8 +90,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     if (!row_ok) qf[t] = bf16x8{};
   }
 
-  const int k0 = split * split_len;
-  const int k1 = min(k0 + split_len, N_k);
+  // 64-bit products: with many splits split * split_len passes 2^31 (such splits are empty)
+  const int k0 = (int)min((long long)split * split_len, (long long)N_k);
+  const int k1 = (int)min((long long)k0 + split_len, (long long)N_k);
   const int nchunks = k0 < k1 ? (k1 - k0 + kDecChunk - 1) / kDecChunk : 0;
   const int min_lim = causal ? N_k - T : N_k - 1;  // smallest per-row limit
   const int my_chunks = nchunks > wave ? (nchunks - wave + 3) / 4 : 0;  // chunks wave, wave+4, ...

@@ -5,7 +5,8 @@ given match the shapes, dtypes and device the C call will assume (the C ABI sees
 raw pointers and cannot check buffer sizes), allocate outputs when none are passed,
 and call the library on the current HIP stream.  Every step of the computation runs in
 the library's HIP kernels; there is no fallback path.  If the library is missing it is
-built once (hipcc); if that fails, or the library cannot be loaded, an error is raised.
+built once (hipcc); if that fails, if the library was built from other sources than the
+ones in the tree, or if it cannot be loaded, an error is raised.
 """
 
 from __future__ import annotations
@@ -13,7 +14,6 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-import sys
 from typing import Optional
 
 import torch
@@ -46,12 +46,11 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     path = library_path()
-    if path == _build.LIB:
-        if not os.path.exists(path):
-            _build.build(verbose=False)
-        elif _build.is_stale():
-            sys.stderr.write(f"warning: {path} is older than its sources; "
-                             "run `python -m online_softmax_07_amd.build`\n")
+    if path == _build.LIB and not os.path.exists(path):
+        _build.build(verbose=False)
+    if _build.is_stale(path):
+        raise RuntimeError(f"{path} was not built from the sources in this tree (missing or mismatched "
+                           f"{os.path.basename(path)}.srchash): run `python -m online_softmax_07_amd.build`")
     L = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]

@@ -2,7 +2,7 @@
 
 FLOPs (page "Attention kernel chains", chain "What FlashAttention removes from HBM"):
 4 * N_q * N_k * d per (batch, query head) -- two matrix products of 2 * N_q * N_k * d
-each -- unchanged by tiling; causal work is counted as half of that.
+each -- the same count whatever the tile sizes; causal work is counted as half of that.
 
 HBM bytes per head with e bytes per value (page "Softmax and FlashAttention", "Maths"):
   standard attention       e * (2Nd + 4N^2 + 2Nd)

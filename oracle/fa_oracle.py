@@ -221,8 +221,8 @@ def split_partials(Q, K, V, scale: float, causal: bool, bounds):
     (O_s normalized by its own sum, lse_s).  An empty range, or a range a row
     cannot see, gives O_s = 0 and lse_s = -inf.
 
-    Attention kernel chains, "The log-sum-exp merge": each worker writes a
-    normalized partial output and its lse.
+    Attention kernel chains, "The log-sum-exp merge": a split's result is its
+    output already divided by its own softmax sum, kept together with that sum's log.
     """
     B, H_q, N_q, d = Q.shape
     _, H_kv, N_k, _ = K.shape

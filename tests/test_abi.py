@@ -20,8 +20,11 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 P = 0x10000  # a fake, 16-byte aligned "device pointer"; never dereferenced (validation fails first)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+CALIB_HEADER = os.path.join(ROOT, "include", "fa_calib.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
 
@@ -42,8 +45,57 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name)
 
 
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["fa.h", "fa_calib.h"]
+
+
+def test_calib_library_exports_every_declared_symbol():
+    from online_softmax_07_amd import calib
+    L = calib.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fabuild.CALIB_LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    names = declared_functions(CALIB_HEADER)
+    assert names == ["fa_calib_clock", "fa_calib_mfma", "fa_calib_stream_read"]
+    for name in names:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_calib_rejects_before_any_launch():
+    from online_softmax_07_amd import calib
+    L = calib.lib()
+    assert L.fa_calib_mfma(None, P, 1, 1, None) == 1
+    assert L.fa_calib_mfma(P, P, 0, 1, None) == 2
+    assert L.fa_calib_mfma(P, P, 1, 0, None) == 2
+    assert L.fa_calib_stream_read(None, 16, P, 1, None) == 1
+    assert L.fa_calib_stream_read(P, 24, P, 1, None) == 2      # not a multiple of 16
+    assert L.fa_calib_stream_read(P + 8, 16, P, 1, None) == 2   # not 16-byte aligned
+    assert L.fa_calib_stream_read(P, 16, P, 0, None) == 2
+    assert L.fa_calib_clock(None, 10, None) == 1
+    assert L.fa_calib_clock(P, 0, None) == 2
+    assert L.fa_calib_clock(P, 10000001, None) == 2
+
+
 def test_build_is_current():
     assert not fabuild.is_stale(), "library is older than its sources: rebuild"
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    """A library whose recorded source hash does not match the tree (built from older
+    sources) is refused by the loader, so no test or bench can run on it."""
+    import shutil
+    lib = tmp_path / "libfa_old.so"
+    shutil.copy(fabuild.LIB, lib)
+    (tmp_path / "libfa_old.so.srchash").write_text("0" * 64 + "\n")
+    monkeypatch.setenv("FA_MI355X_LIB", str(lib))
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built from the sources"):
+        fa.lib()
+    # the same file with the tree's hash (and the defines it was built with) is accepted
+    (tmp_path / "libfa_old.so.srchash").write_text(fabuild.source_hash(["FA_TEST_DEFINE=1"]) + " FA_TEST_DEFINE=1\n")
+    assert not fabuild.is_stale(str(lib))
+    (tmp_path / "libfa_old.so.srchash").unlink()
+    assert fabuild.is_stale(str(lib))
 
 
 def test_version_and_status_strings():
@@ -157,6 +209,9 @@ def dec(**kw):
     (dict(K=P + 4), fa.FA_ERR_ALIGNMENT), (dict(bt=P + 2, ps=16, pps=7), fa.FA_ERR_ALIGNMENT),
     (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE), (dict(ns=0, N_k=100000, wsb=10), fa.FA_ERR_WORKSPACE),
     (dict(ws=P + 4), fa.FA_ERR_ALIGNMENT),
+    # a split count whose partial rows (splits x B*H_q*T) pass 2^31: rejected before any
+    # workspace size is computed (those offsets, and split * split_len, would wrap)
+    (dict(ns=(1 << 29) + 1), fa.FA_ERR_BAD_SHAPE), (dict(ns=0x7fffffff, wsb=(1 << 63)), fa.FA_ERR_BAD_SHAPE),
 ])
 def test_decode_rejects(kw, status):
     assert dec(**kw) == status
@@ -204,6 +259,7 @@ def test_workspace_and_split_sizes():
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 1) == 0
     # ns partial rows of d fp32 plus ns lse values, each part rounded to 256 bytes
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == 8 * 32 * 128 * 4 + 1024
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, (1 << 26) + 1) == 0   # 32 rows x splits > 2^31
     assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == 4 * 512 * 128 * 4 + 4 * 512 * 4
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 8 * 32 * 128 * 4 + 1024  # empty cache, 8 splits
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, -1, 128, 8) == 0                      # invalid length
