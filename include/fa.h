@@ -6,7 +6,8 @@
  * DEVICE pointer owned by the caller.  The library never allocates, frees or synchronises:
  * each call validates its arguments, enqueues its kernels on `stream` and returns.  Outputs
  * are valid once the stream reaches the enqueued work; inputs must stay alive until then.
- * There is no global mutable state, so calls from several host threads are safe.
+ * There is no global mutable state (except the scratch of fa_decode_splitkv_noalloc, below),
+ * so calls from several host threads are safe.
  *
  * Layouts (all contiguous, head dimension fastest, as the Flash Attention 1 kernel of the
  * page "Kernel visualization: Flash Attention 1" ("Initial setup") offsets its pointers by
@@ -192,6 +193,30 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
                       float scale, int causal, int num_splits,
                       const int32_t* block_table, int page_size, int pages_per_seq,
                       void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_decode_splitkv_noalloc -- fa_decode_splitkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, with the partial results kept in
+ * a scratch array of FA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on
+ * each GPU it runs on until the process ends, instead of a caller's workspace.
+ *
+ *   Arguments as fa_decode_splitkv without the workspace.  A call whose partials need more
+ *   than FA_DECODE_NOALLOC_SCRATCH_BYTES (fa_decode_workspace_bytes(...) of its sizes and
+ *   split count) returns FA_ERR_WORKSPACE and enqueues nothing; FA_ERR_HIP if the scratch
+ *   address cannot be looked up.  Nothing here calls hipMalloc or hipFree; the first call
+ *   on a GPU looks up that GPU's copy of the array (hipGetSymbolAddress) once.
+ *   Every split writes all of its partial rows before the merge reads them, so the scratch
+ *   keeps no state from one call to the next that matters.  All calls on one GPU share its
+ *   scratch: calls that may overlap in time on one GPU (different streams, or several
+ *   host threads without ordering) race and must not be made.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              int B, int H_q, int H_kv, int T, int N_k, int d,
+                              float scale, int causal, int num_splits,
+                              const int32_t* block_table, int page_size, int pages_per_seq,
+                              int dtype, void* stream);
 
 /*
  * fa_lse_merge -- combine normalized partial results over disjoint key sets.

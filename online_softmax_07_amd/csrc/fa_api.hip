@@ -3,6 +3,8 @@
 // runs before the first HIP call, so an invalid call enqueues nothing.
 #include <math.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
 
@@ -151,10 +153,21 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
   return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float));
 }
 
-int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q,
-                      int H_kv, int T, int N_k, int d, float scale, int causal, int num_splits,
-                      const int32_t* block_table, int page_size, int pages_per_seq, void* workspace,
-                      size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+// The partial results of fa_decode_splitkv_noalloc: one array per GPU, resident for the
+// process's lifetime, shared by every call on that GPU.  In host code its name is only a
+// stand-in: the device address of each GPU's copy comes from hipGetSymbolAddress
+// (scratch_on below), and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Validation shared by both decode entry points; on FA_OK, *ns_out holds the resolved split
+// count and *need_out the partial-result bytes it takes (0 with one split).
+int check_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv,
+                 int T, int N_k, int d, float scale, int causal, int num_splits, const int32_t* block_table,
+                 int page_size, int pages_per_seq, int dtype, int* ns_out, size_t* need_out) {
   if (!present(Q, T > 0) || !present(O, T > 0) || !present(K, N_k > 0) || !present(V, N_k > 0))
     return FA_ERR_NULL_PTR;
   int st = check_heads(B, H_q, H_kv, T, N_k, d);
@@ -173,11 +186,17 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
   const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
   // every partial row index (split * rows + row) must fit 32 bits, as in fa_lse_merge
   if (ns > 1 && (long long)ns * B * H_q * T > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
-  const size_t need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
-  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGNMENT;
-  if (T == 0) return FA_OK;  // no query: nothing to write (N_k == 0: O = 0, LSE = -inf)
+  *ns_out = ns;
+  *need_out = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
+  return FA_OK;
+}
 
+// Launch the split kernel and, with more than one split, the merge, with the partials in
+// `workspace` (laid out as fa_decode_workspace_bytes describes).
+int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q, int H_kv, int T,
+               int N_k, int d, float scale, int causal, int ns, const int32_t* block_table, int page_size,
+               int pages_per_seq, void* workspace, int dtype, void* stream) {
+  if (T == 0) return FA_OK;  // no query: nothing to write (N_k == 0: O = 0, LSE = -inf)
   const size_t rows = (size_t)B * H_q * T;
   float* O_part = nullptr;
   float* LSE_part = nullptr;
@@ -192,6 +211,70 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
   if (e != hipSuccess) return FA_ERR_HIP;
   if (ns > 1) e = fa::launch_lse_merge(O_part, LSE_part, O, LSE, ns, (int)rows, d, out_f32, stream);
   return status_of(e);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU `stream` belongs to (the current GPU for a NULL
+// stream), looked up once per GPU with that GPU current.  NULL on any HIP error.
+void* scratch_on(void* stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q,
+                      int H_kv, int T, int N_k, int d, float scale, int causal, int num_splits,
+                      const int32_t* block_table, int page_size, int pages_per_seq, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  int ns = 0;
+  size_t need = 0;
+  const int st = check_decode(Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, num_splits, block_table,
+                              page_size, pages_per_seq, dtype, &ns, &need);
+  if (st != FA_OK) return st;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGNMENT;
+  return run_decode(Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, ns, block_table, page_size,
+                    pages_per_seq, workspace, dtype, stream);
+}
+
+int fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H_q,
+                              int H_kv, int T, int N_k, int d, float scale, int causal, int num_splits,
+                              const int32_t* block_table, int page_size, int pages_per_seq, int dtype,
+                              void* stream) {
+  int ns = 0;
+  size_t need = 0;
+  const int st = check_decode(Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, num_splits, block_table,
+                              page_size, pages_per_seq, dtype, &ns, &need);
+  if (st != FA_OK) return st;
+  if (need > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  if (T == 0) return FA_OK;
+  void* ws = nullptr;
+  if (need > 0 && (ws = scratch_on(stream)) == nullptr) return FA_ERR_HIP;
+  return run_decode(Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, ns, block_table, page_size,
+                    pages_per_seq, ws, dtype, stream);
 }
 
 int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE, int num_splits, int rows,

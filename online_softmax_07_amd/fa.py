@@ -24,7 +24,8 @@ FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, 
 FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
 
 EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-            "fa_lse_merge", "fa_status_string", "fa_version")
+            "fa_decode_splitkv_noalloc", "fa_lse_merge", "fa_status_string", "fa_version")
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_DECODE_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.restype = sz
     L.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, i, vp, sz, i, vp]
     L.fa_decode_splitkv.restype = i
+    L.fa_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, i, i, vp]
+    L.fa_decode_splitkv_noalloc.restype = i
     L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     L.fa_lse_merge.restype = i
     L.fa_status_string.argtypes = [i]
@@ -263,16 +266,8 @@ def fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits) -> int:
     return int(lib().fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits))
 
 
-def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None,
-                      lse: Optional[torch.Tensor] = None, *, causal: bool = True,
-                      scale: Optional[float] = None, num_splits: int = 0,
-                      block_table: Optional[torch.Tensor] = None, n_k: Optional[int] = None,
-                      workspace: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                      want_lse: bool = True, check_table: bool = True, stream=None):
-    """Split-KV decode.  q [B,H_q,T,d] bf16.  Contiguous: k, v [B,H_kv,N_k,d].  Paged:
-    k, v pools [num_pages,page_size,H_kv,d] with block_table [B,pages_per_seq] int32 and
-    ``n_k`` tokens per sequence (default pages_per_seq*page_size).  With ``check_table``
-    the table entries are checked to lie inside the pool (one device reduction)."""
+def _decode_prelude(q, k, v, o, lse, block_table, n_k, out_dtype, want_lse, check_table):
+    """Shapes and outputs shared by both decode entry points."""
     _need(q.dim() == 4 and q.dtype == torch.bfloat16, "q must be bf16 [B,H_q,T,d]")
     B, H_q, T, d = q.shape
     _need(k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16 and k.shape == v.shape and k.dim() == 4,
@@ -294,6 +289,21 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Opti
         lse = torch.empty((B, H_q, T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse.shape == (B, H_q, T) and lse.dtype == torch.float32, "lse must be fp32 [B,H_q,T]")
+    return B, H_q, H_kv, T, N_k, d, page_size, pages_per_seq, dtype, o, lse
+
+
+def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, *, causal: bool = True,
+                      scale: Optional[float] = None, num_splits: int = 0,
+                      block_table: Optional[torch.Tensor] = None, n_k: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      want_lse: bool = True, check_table: bool = True, stream=None):
+    """Split-KV decode.  q [B,H_q,T,d] bf16.  Contiguous: k, v [B,H_kv,N_k,d].  Paged:
+    k, v pools [num_pages,page_size,H_kv,d] with block_table [B,pages_per_seq] int32 and
+    ``n_k`` tokens per sequence (default pages_per_seq*page_size).  With ``check_table``
+    the table entries are checked to lie inside the pool (one device reduction)."""
+    B, H_q, H_kv, T, N_k, d, page_size, pages_per_seq, dtype, o, lse = _decode_prelude(
+        q, k, v, o, lse, block_table, n_k, out_dtype, want_lse, check_table)
     need = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, num_splits)
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -308,6 +318,26 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Opti
                                  int(page_size), int(pages_per_seq), _ptr(workspace), ws_bytes, dtype,
                                  _stream(stream, q.device))
     _raise(st, "fa_decode_splitkv")
+    return o, lse
+
+
+def fa_decode_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                              lse: Optional[torch.Tensor] = None, *, causal: bool = True,
+                              scale: Optional[float] = None, num_splits: int = 0,
+                              block_table: Optional[torch.Tensor] = None, n_k: Optional[int] = None,
+                              check_table: bool = False, stream=None):
+    """fa_decode_splitkv with the partials in the library's per-GPU scratch: the caller
+    passes every output (``o``, and ``lse`` or None) and nothing is allocated on the way."""
+    _need(o is not None, "o must be given (this entry point allocates nothing)")
+    B, H_q, H_kv, T, N_k, d, page_size, pages_per_seq, dtype, o, lse = _decode_prelude(
+        q, k, v, o, lse, block_table, n_k, None, False, check_table)
+    _check_dev(q.device, q=q, k=k, v=v, o=o, lse=lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H_q, H_kv, T, N_k, d,
+                                         float(scale), int(bool(causal)), int(num_splits), _ptr(block_table),
+                                         int(page_size), int(pages_per_seq), dtype, _stream(stream, q.device))
+    _raise(st, "fa_decode_splitkv_noalloc")
     return o, lse
 
 

@@ -217,6 +217,34 @@ def test_decode_rejects(kw, status):
     assert dec(**kw) == status
 
 
+def dec_noalloc(**kw):
+    a = dict(Q=P, K=P, V=P, O=P, LSE=P, B=1, H_q=4, H_kv=2, T=1, N_k=100, d=128, scale=0.1, causal=1, ns=4,
+             bt=None, ps=0, pps=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_decode_splitkv_noalloc(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H_q"],
+                                              a["H_kv"], a["T"], a["N_k"], a["d"], a["scale"], a["causal"],
+                                              a["ns"], a["bt"], a["ps"], a["pps"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), fa.FA_ERR_NULL_PTR), (dict(T=-1), fa.FA_ERR_BAD_SHAPE), (dict(H_q=5), fa.FA_ERR_BAD_SHAPE),
+    (dict(ns=-1), fa.FA_ERR_BAD_SHAPE), (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(K=P + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(ns=(1 << 29) + 1), fa.FA_ERR_BAD_SHAPE),
+    # partials beyond the 16 MiB scratch: 8193 splits x 4 rows x 129 floats
+    (dict(ns=8193), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects(kw, status):
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_scratch_limit():
+    rows, d = 4, 128
+    assert fa.fa_decode_workspace_bytes(1, 4, 2, 1, 100, d, 8193) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_bytes(1, 4, 2, 1, 100, d, 8000) <= fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert "FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)" in open(HEADER).read()
+    assert dec_noalloc(T=0) == fa.FA_OK          # no query row: validated no-op, no HIP call
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(Op=None), fa.FA_ERR_NULL_PTR), (dict(Lp=None), fa.FA_ERR_NULL_PTR), (dict(O=None), fa.FA_ERR_NULL_PTR),
     (dict(ns=0), fa.FA_ERR_BAD_SHAPE), (dict(rows=-1), fa.FA_ERR_BAD_SHAPE), (dict(d=0), fa.FA_ERR_BAD_SHAPE),

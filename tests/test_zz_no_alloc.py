@@ -1,0 +1,76 @@
+"""fa_decode_splitkv_noalloc (partials in the library's per-GPU scratch) against
+fa_decode_splitkv (partials in a caller's workspace) and the fp64 oracle, through the C
+ABI: two calls in a row on the same GPU, the second with a smaller input, so the second
+reads a scratch that still holds the first call's partials."""
+
+import pytest
+import torch
+
+import oracle.fa_oracle as orc
+from online_softmax_07_amd import fa, workloads
+from parity import check_lse, check_o
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def host(t):
+    return t.float().numpy()
+
+
+def both(w, ns, out_dtype):
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    bt = None if w.block_table is None else w.block_table.to(DEV)
+    o_ws = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
+    l_ws = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_decode_splitkv(q, k, v, o_ws, l_ws, causal=w.causal, scale=w.scale, num_splits=ns, block_table=bt,
+                         n_k=w.n_k)
+    torch.cuda.synchronize()
+    o_na = torch.full(q.shape, float("nan"), dtype=out_dtype, device=DEV)
+    l_na = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    fa.fa_decode_splitkv_noalloc(q, k, v, o_na, l_na, causal=w.causal, scale=w.scale, num_splits=ns,
+                                 block_table=bt, n_k=w.n_k)
+    torch.cuda.synchronize()
+    return (o_ws, l_ws), (o_na, l_na)
+
+
+def check(w, ns, out_dtype):
+    say(w.name, "num_splits", ns, out_dtype)
+    (o_ws, l_ws), (o_na, l_na) = both(w, ns, out_dtype)
+    # same kernels, same split count: the results agree bit for bit
+    assert torch.equal(o_na, o_ws) and torch.equal(l_na, l_ws)
+    bt = None if w.block_table is None else w.block_table.numpy()
+    O, L = orc.decode(host(w.q), host(w.k), host(w.v), w.scale, w.causal, block_table=bt,
+                      page_size=w.page_size or None, n_k=w.n_k)
+    check_o(o_na, O, "bf16" if out_dtype == torch.bfloat16 else "fp32out")
+    check_lse(l_na, L)
+
+
+def test_noalloc_two_calls_second_smaller():
+    # first: the split-KV workload (1 x 32 query / 8 KV heads, 131072 cached keys), 64 splits
+    big = workloads.decode_splitkv_128k()
+    check(big, 64, torch.bfloat16)
+    # second, smaller: a paged cache of 4 sequences x 1000 tokens, 8 / 1 heads, 4 splits
+    small = workloads.decode(4, 8, 1, 1, 1000, 128, seed=77, causal=True, page_size=16, num_pages=4 * 63 + 9)
+    check(small, 4, torch.float32)
+
+
+def test_noalloc_automatic_splits_and_repeat():
+    w = workloads.decode(2, 16, 4, 3, 5000, 64, seed=78, causal=True)
+    for _ in range(2):
+        check(w, 0, torch.bfloat16)
+
+
+def test_noalloc_over_the_scratch_is_refused():
+    w = workloads.decode(1, 32, 8, 1, 4096, 128, seed=79, causal=True)
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    o = torch.empty_like(q)
+    ns = 2000   # 2000 splits x 32 rows x 129 floats > 16 MiB
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 4096, 128, ns) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_decode_splitkv_noalloc(q, k, v, o, None, causal=True, scale=w.scale, num_splits=ns)
+    assert e.value.status == fa.FA_ERR_WORKSPACE
