@@ -42,6 +42,30 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
+// Launch shape and schedule options, fixed at build time.  The shipped values are the
+// defaults; the others are built on demand to compare tile shapes and workgroup orders.
+#ifndef FA_FWD_D128_WAVES
+#define FA_FWD_D128_WAVES 8      // d = 128: waves of 32 query rows per workgroup (Br = 32 x waves)
+#endif
+#ifndef FA_FWD_D128_BC
+#define FA_FWD_D128_BC 128       // d = 128, contiguous K/V: keys per K/V tile
+#endif
+#ifndef FA_FWD_XCD_MAP
+#define FA_FWD_XCD_MAP 1         // 1: each XCD walks its own heads; 0: plain blockIdx order
+#endif
+#ifndef FA_FWD_D128_VPF
+#define FA_FWD_D128_VPF 1        // d = 128: key steps of V^T fragments read ahead of their MFMAs
+#endif
+#ifndef FA_FWD_D64_VPF
+#define FA_FWD_D64_VPF 1         // d = 64: the same
+#endif
+#ifndef FA_FWD_D128_VEARLY
+#define FA_FWD_D128_VEARLY 0     // d = 128, 1: the first of those reads are issued before the softmax
+#endif
+#ifndef FA_FWD_D64_VEARLY
+#define FA_FWD_D64_VEARLY 1      // d = 64: the same (+3 % causal)
+#endif
+
 namespace fa {
 
 // NW waves of RH x 32 query rows per workgroup, BR = 256 rows in both launches, two waves
@@ -94,7 +118,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
   const int wg = blockIdx.x;
   const int n_bh = total_wg / n_units;
   int bh, unit;
-  if ((n_bh & 7) == 0) {
+  if (!FA_FWD_XCD_MAP) {
+    bh = wg / n_units;
+    unit = wg % n_units;
+  } else if ((n_bh & 7) == 0) {
     const int hpx = n_bh >> 3;            // heads per XCD
     const int x = wg & 7, idx = wg >> 3;  // XCD, and position in its dispatch order
     bh = x * hpx + idx / n_units;
@@ -312,6 +339,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
         }
 
         __builtin_amdgcn_s_setprio(0);
+        // ---- V^T fragments through transposing LDS reads, VP key steps ahead of the PV
+        // MFMAs that use them; the first VEARLY steps are requested before the softmax, so
+        // their LDS latency hides behind it ----
+        auto vfrag = [&](int u, int cb) {
+          const __bf16* p = vs + 16 * u * D;
+          return join_bf16x8(lds_read_tr16(p + voff[0][cb]), lds_read_tr16(p + voff[1][cb]));
+        };
+        constexpr int VP = D == 64 ? FA_FWD_D64_VPF : FA_FWD_D128_VPF;
+        // (not for the paged variant, whose table addressing leaves no registers for it)
+        constexpr int VEARLY = (!PAGED && (D == 64 ? FA_FWD_D64_VEARLY : FA_FWD_D128_VEARLY)) ? VP : 0;
+        bf16x8 vf[VP + 1][T::NCB];
+#pragma unroll
+        for (int u = 0; u < VEARLY; ++u)
+#pragma unroll
+          for (int cb = 0; cb < T::NCB; ++cb) vf[u][cb] = vfrag(u, cb);
         bf16x8 pf[RH][BC / 16];
 #pragma unroll
         for (int x = 0; x < RH; ++x) {
@@ -373,25 +415,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(
           for (int u = 0; u < BC / 16; ++u) lb_run[x] = sum_bf16x8(pf[x][u], lb_run[x]);
         }
 
-        // ---- O^T += V_j^T P^T: V^T fragments through transposing LDS reads ----
-        auto vfrag = [&](int u, int cb) {
-          const __bf16* p = vs + 16 * u * D;
-          return join_bf16x8(lds_read_tr16(p + voff[0][cb]), lds_read_tr16(p + voff[1][cb]));
-        };
-        bf16x8 vf[2][T::NCB];
+        // ---- O^T += V_j^T P^T ----
 #pragma unroll
-        for (int cb = 0; cb < T::NCB; ++cb) vf[0][cb] = vfrag(0, cb);
+        for (int u = VEARLY; u < VP; ++u)
+#pragma unroll
+          for (int cb = 0; cb < T::NCB; ++cb) vf[u][cb] = vfrag(u, cb);
         __builtin_amdgcn_s_setprio(1);  // MFMA section: issue ahead of the other wave on this SIMD
 #pragma unroll
         for (int u = 0; u < BC / 16; ++u) {
-          if (u + 1 < BC / 16) {
+          if (u + VP < BC / 16) {
 #pragma unroll
-            for (int cb = 0; cb < T::NCB; ++cb) vf[(u + 1) & 1][cb] = vfrag(u + 1, cb);
+            for (int cb = 0; cb < T::NCB; ++cb) vf[(u + VP) % (VP + 1)][cb] = vfrag(u + VP, cb);
           }
 #pragma unroll
           for (int cb = 0; cb < T::NCB; ++cb)
 #pragma unroll
-            for (int x = 0; x < RH; ++x) o[x][cb] = mfma32x32x16(vf[u & 1][cb], pf[x][u], o[x][cb]);
+            for (int x = 0; x < RH; ++x) o[x][cb] = mfma32x32x16(vf[u % (VP + 1)][cb], pf[x][u], o[x][cb]);
         }
         __builtin_amdgcn_s_setprio(0);
       } else {
@@ -496,7 +535,7 @@ static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_
   // 32-row halves, so each K or V fragment read from LDS feeds two MFMAs; the registers
   // this takes fit at d = 64 only
   constexpr int RH = D == 64 ? 2 : 1;
-  constexpr int NW = RH == 2 ? 4 : 8;
+  constexpr int NW = RH == 2 ? 4 : (PAGED ? 8 : FA_FWD_D128_WAVES);
   constexpr int BR = FwdTile<D, BC, NW, RH>::BR;
   const int n_qblocks = (a.N_q + BR - 1) / BR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
@@ -515,7 +554,7 @@ static hipError_t dispatch_out(const FwdArgs& a, bool out_f32, const int32_t* bt
   // key tile: 128 keys for contiguous K/V at d = 128 (half the barriers per key); 64 keys for
   // the paged variant at d = 128 (its per-lane page addressing would not fit the registers
   // otherwise) and at d = 64 (two row halves per wave)
-  constexpr int BC = (D == 128 && !PAGED) ? 128 : 64;
+  constexpr int BC = (D == 128 && !PAGED) ? FA_FWD_D128_BC : 64;
   if (a.causal)
     return out_f32 ? launch<D, BC, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC, true, PAGED, __bf16>(a, bt, ps, pps);
   return out_f32 ? launch<D, BC, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC, false, PAGED, __bf16>(a, bt, ps, pps);

@@ -2,6 +2,8 @@
 
     python -m online_softmax_07_amd.profiling --workload long_prefill_8192 [--workload ...]
         [--raw gpurun_out/prof] [--summaries gpurun_out/prof/summaries] [--steps 20] [--warmup 5]
+        [--variant br128 --passes trace,fetch,write]
+    python -m online_softmax_07_amd.profiling --next3-table      # measured vs modelled bytes
 
 For each workload this runs bench.py (timing that workload only) as a child process under
 rocprofv3, once per pass:
@@ -155,11 +157,11 @@ def _bench_cmd(workload, steps, warmup, extra=()):
             "--steps", str(steps), "--warmup", str(warmup), *extra]
 
 
-def _run(cmd, log, limit):
+def _run(cmd, log, limit, env=None):
     print("+", " ".join(cmd), flush=True)
     with open(log, "w") as f:
         r = subprocess.run(["timeout", "-s", "KILL", str(limit), *cmd], stdout=f, stderr=subprocess.STDOUT,
-                           cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp"})
+                           cwd="/tmp", env={**(env or os.environ), "TMPDIR": "/tmp"})
     if r.returncode != 0:
         with open(log) as f:
             tail = f.read()[-3000:]
@@ -180,9 +182,21 @@ def _last_json(path):
     return json.loads(line) if line else None
 
 
-def profile(workload, raw, summaries, steps, warmup, limit=240, run=True):
+def profile(workload, raw, summaries, steps, warmup, limit=240, run=True, variant=None,
+            passes=("trace", "fetch", "write", "mfma")):
     name, title, prefixes, family, alg_bytes, flops = CASES[workload]
-    base = os.path.join(raw, workload)
+    env = None
+    defines = []
+    if variant is not None:
+        lib = fb.variant_lib(variant)
+        defines = fb.VARIANTS[variant]
+        env = {**os.environ, "FA_MI355X_LIB": lib}
+        name = f"next3_{variant}_{name}"
+        title = f"{title}; build variant {variant} ({' '.join('-D' + d for d in defines)})"
+        workload_dir = f"{variant}_{workload}"
+    else:
+        workload_dir = workload
+    base = os.path.join(raw, workload_dir)
     os.makedirs(base, exist_ok=True)
     os.makedirs(summaries, exist_ok=True)
     rel = os.path.relpath
@@ -194,17 +208,18 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True):
     cmds["trace"] = ["rocprofv3", "--kernel-trace", "--stats", "-d", tdir, "-o", "t", "--",
                      *_bench_cmd(workload, steps, warmup, ["--out", tjson])]
     if run:
-        _run(cmds["trace"], os.path.join(base, "trace.log"), limit)
+        _run(cmds["trace"], os.path.join(base, "trace.log"), limit, env)
     # counters
     for key, pmc in (("fetch", ["FETCH_SIZE"]), ("write", ["WRITE_SIZE"]),
-                     *((("mfma", MFMA_COUNTERS),) if family in ("prefill", "backward") else ())):
+                     *((("mfma", MFMA_COUNTERS),) if family in ("prefill", "backward") and "mfma" in passes else ())):
         cmds[key] = ["rocprofv3", "--pmc", *pmc, "-d", os.path.join(base, key), "-o", "t", "--",
                      *_bench_cmd(workload, 3, 1, ["--calib-copy"] if key in ("fetch", "write") else [])]
         if run:
-            _run(cmds[key], os.path.join(base, key + ".log"), limit)
+            _run(cmds[key], os.path.join(base, key + ".log"), limit, env)
 
     def show(cmd):
-        return " ".join(rel(c, ROOT) if c.startswith(ROOT) else c for c in cmd)
+        text = " ".join(rel(c, ROOT) if c.startswith(ROOT) else c for c in cmd)
+        return (f"FA_MI355X_LIB={rel(fb.variant_lib(variant), ROOT)} " + text) if variant else text
 
     # ---- trace summary ----
     bench = _last_json(tjson)
@@ -220,7 +235,8 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True):
     scale = 1e9 if family == "decode" else 1e12
     lines = [f"# {title}", "",
              "Produced by (from the repository root, one MI355X):", "",
-             f"    python -m online_softmax_07_amd.profiling --workload {workload} --steps {steps} --warmup {warmup}",
+             f"    python -m online_softmax_07_amd.profiling --workload {workload} --steps {steps} --warmup {warmup}"
+             + (f" --variant {variant} --passes {','.join(passes)}" if variant else ""),
              "", "which runs, each as its own process:", ""]
     lines += [f"    {show(c)}" for c in cmds.values()]
     lines += ["", f"## Kernel trace ({bench['warmup']} warm-up calls, then {n_timed} timed calls)", "",
@@ -258,6 +274,7 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True):
          "fetch_scale": ff, "write_scale": wf,
          "traffic_bytes_per_launch": round(traffic), "algorithmic_bytes_per_launch": round(alg_bytes),
          "traffic_over_algorithmic": round(traffic / alg_bytes, 4),
+         "variant": variant, "defines": defines, "mean_launch_us": round(timed_us, 2),
          "commands": [show(cmds["fetch"]), show(cmds["write"])]}
     with open(os.path.join(summaries, f"traffic_{name}.json"), "w") as f:
         json.dump(t, f, indent=1)
@@ -289,7 +306,45 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True):
           flush=True)
 
 
+NEXT3_WORKLOADS = {   # bench name -> (B, H, N, d, causal)
+    "prefill_d128_causal": (4, 16, 4096, 128, True),
+    "prefill_d128_full": (4, 16, 4096, 128, False),
+    "long_prefill_8192": (1, 32, 8192, 128, True),
+}
+NEXT3_BR = {None: 256, "br256_plain": 256, "br128": 128, "br64": 64}
+
+
+def next3_table(profiles_dir) -> str:
+    """Markdown table of measured against modelled HBM bytes per prefill launch, from the
+    committed traffic summaries of the shipped build and its variants: the no-reuse model of
+    page "Softmax and FlashAttention" ("Maths"), counted per query block (exact under the
+    causal mask), and the every-value-once floor."""
+    rows = ["| variant | Br | workload | model, no reuse (MB) | measured (MB) | floor (MB) | measured / floor | "
+            "mean launch (us) | TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for variant, br in NEXT3_BR.items():
+        for wl, (B, H, N, d, causal) in NEXT3_WORKLOADS.items():
+            name = CASES[wl][0] if variant is None else f"next3_{variant}_{CASES[wl][0]}"
+            path = os.path.join(profiles_dir, f"traffic_{name}.json")
+            if not os.path.exists(path):
+                continue
+            with open(path) as f:
+                t = json.load(f)
+            model = B * H * rl.flash_bytes_model(N, N, d, br, causal)
+            floor = rl.prefill_bytes_floor(B, H, H, N, N, d)
+            meas = t["traffic_bytes_per_launch"]
+            us = t.get("mean_launch_us")
+            tf = f"{rl.prefill_flops(B, H, N, N, d, causal) / (us * 1e-6) / 1e12:.0f}" if us else "-"
+            label = "shipped (XCD order)" if variant is None else (
+                "plain blockIdx order" if variant.endswith("plain") else "XCD order")
+            rows.append(f"| {variant or 'br256'}: {label} | {br} | {CASES[wl][0]} | {model / 1e6:.1f} | "
+                        f"{meas / 1e6:.1f} | {floor / 1e6:.1f} | {meas / floor:.2f} | {us if us else '-'} | {tf} |")
+    return "\n".join(rows)
+
+
 def main():
+    if "--next3-table" in sys.argv:
+        print(next3_table(os.path.join(ROOT, "profiles")))
+        return 0
     p = argparse.ArgumentParser()
     p.add_argument("--workload", action="append", required=True, choices=sorted(CASES))
     p.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
@@ -298,9 +353,13 @@ def main():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--summarize-only", action="store_true",
                    help="write the summaries from the results already under --raw (no profiling run)")
+    p.add_argument("--variant", choices=sorted(fb.VARIANTS), default=None,
+                   help="profile a build variant (python -m online_softmax_07_amd.build --variants)")
+    p.add_argument("--passes", default="trace,fetch,write,mfma")
     a = p.parse_args()
     for w in a.workload:
-        profile(w, a.raw, a.summaries, a.steps, a.warmup, run=not a.summarize_only)
+        profile(w, a.raw, a.summaries, a.steps, a.warmup, run=not a.summarize_only, variant=a.variant,
+                passes=tuple(a.passes.split(",")))
     print("profiling done", flush=True)
 
 

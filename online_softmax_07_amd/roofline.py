@@ -63,6 +63,23 @@ def flash_bytes_floor(N, d, e=2) -> float:
     return 4.0 * e * N * d
 
 
+def flash_bytes_model(N_q, N_k, d, Br, causal, e=2, lse=True) -> float:
+    """HBM bytes of one (batch, head) under the no-cache-reuse model of the FlashAttention-2
+    loop order: Q and O once, and K and V read once per query block of Br rows.  Without the
+    mask every block reads all N_k keys, which is e(2Nd + 2N^2 d / Br) for N_q = N_k = N;
+    with the bottom-right causal mask block i (rows i Br ..) reads only the keys its last
+    row sees, counted exactly.  Plus the fp32 LSE when `lse`."""
+    n_blocks = -(-N_q // Br)
+    kv_rows = 0
+    for i in range(n_blocks):
+        last_row = min((i + 1) * Br, N_q) - 1
+        kv_rows += N_k if not causal else max(0, min(N_k, last_row + (N_k - N_q) + 1))
+    b = e * (2.0 * N_q * d + 2.0 * kv_rows * d)
+    if lse:
+        b += 4.0 * N_q
+    return b
+
+
 def decode_bytes(B, H_q, H_kv, T, N_k, d, pages_per_seq=0, e=2) -> float:
     kv = 2.0 * B * H_kv * N_k * d * e
     qo = 2.0 * B * H_q * T * d * e

@@ -26,14 +26,34 @@ def test_visible_pairs_brute_force(n_q, n_k, causal):
 
 
 def test_flop_conventions():
-    # the prefill metric halves causal work; exact pair counting is one N(N+1)/2 * 4d per head
-    assert rl.prefill_flops(4, 16, 4096, 4096, 128, True) == 4.0 * 4096 * 4096 * 128 * 64 / 2
-    assert rl.chunked_prefill_flops(1, 1, 3, 3, 8, True) == 4 * 8 * 6
-    assert rl.chunked_prefill_flops(1, 1, 2, 5, 8, True) == 4 * 8 * (4 + 5)
-    # decode bytes: K and V once per KV head, plus Q, O, LSE and the table
-    assert rl.decode_bytes(1, 32, 8, 1, 131072, 128) == 536887424
-    assert rl.decode_bytes(64, 8, 1, 1, 8192, 128, pages_per_seq=512) == 268830720
-    assert rl.prefill_bytes_floor(4, 16, 16, 4096, 4096, 128) == 269484032
+    # the metric: causal prefill work is half the full product count (the pages' 4 N^2 d per
+    # head is pinned to the printed 34.4 GFLOP in test_traffic_model.py)
+    assert rl.prefill_flops(4, 16, 4096, 4096, 128, True) * 2 == rl.prefill_flops(4, 16, 4096, 4096, 128, False)
+    # chunked prefill counts 4 d per visible (query, key) pair: brute-force pair counts
+    for n_q, n_k in ((3, 3), (2, 5), (5, 2), (7, 19), (0, 4)):
+        pairs = sum(1 for i in range(n_q) for j in range(n_k) if j <= i + n_k - n_q)
+        assert rl.chunked_prefill_flops(1, 1, n_q, n_k, 8, True) == 4 * 8 * pairs
+        assert rl.visible_pairs(n_q, n_k, True) == pairs
+    assert rl.chunked_prefill_flops(2, 3, 7, 19, 8, False) == 4 * 8 * 7 * 19 * 6
+
+
+def test_byte_conventions_from_the_workload_tensors():
+    """Algorithmic bytes = every input read once and every output written once, summed
+    from the actual tensors of each workload (O has Q's shape; LSE one fp32 per row)."""
+    def nbytes(t):
+        return t.numel() * t.element_size()
+    w = workloads.decode_splitkv_128k()
+    rows = w.q.shape[0] * w.q.shape[1] * w.q.shape[2]
+    assert rl.decode_bytes(1, 32, 8, 1, 131072, 128) == nbytes(w.k) + nbytes(w.v) + 2 * nbytes(w.q) + 4 * rows
+    w = workloads.decode_paged_b64()
+    rows = w.q.shape[0] * w.q.shape[1] * w.q.shape[2]
+    # every page of the pool belongs to some sequence here, so the pool is the K/V read once
+    assert w.block_table.numel() * w.page_size == w.k.shape[0] * w.k.shape[1]
+    assert rl.decode_bytes(64, 8, 1, 1, 8192, 128, pages_per_seq=512) == (
+        nbytes(w.k) + nbytes(w.v) + 2 * nbytes(w.q) + 4 * rows + nbytes(w.block_table))
+    w = workloads.prefill_4x16x4096(128, True)
+    rows = w.q.shape[0] * w.q.shape[1] * w.q.shape[2]
+    assert rl.prefill_bytes_floor(4, 16, 16, 4096, 4096, 128) == nbytes(w.k) + nbytes(w.v) + 2 * nbytes(w.q) + 4 * rows
 
 
 def test_inputs_are_seeded_and_bf16_exact():
