@@ -22,12 +22,19 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 // A tensor of zero elements may be passed as NULL; any other must not.
 bool present(const void* p, bool nonempty) { return p != nullptr || !nonempty; }
 
+// a * b * c <= 2^31 - 1 for non-negative ints, without overflowing along the way
+bool product_fits31(long long a, long long b, long long c) {
+  const long long lim = 0x7fffffffLL;
+  if (a == 0 || b == 0 || c == 0) return true;
+  return a <= lim / b && a * b <= lim / c;
+}
+
 // Sizes: B, heads and d at least 1; the sequence lengths may be 0 (empty inputs).
 int check_heads(int B, int H_q, int H_kv, int n_q, int n_k, int d) {
   if (B < 1 || H_q < 1 || H_kv < 1 || n_q < 0 || n_k < 0 || d < 1) return FA_ERR_BAD_SHAPE;
   if (H_q % H_kv != 0) return FA_ERR_BAD_SHAPE;
-  // every element index must fit the 64-bit offsets and every row index a 32-bit int
-  if ((long long)B * H_q * n_q > 0x7fffffffLL || (long long)B * H_kv * n_k > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  // every row index (B*H*N) must fit a 32-bit int; the element offsets are 64-bit
+  if (!product_fits31(B, H_q, n_q) || !product_fits31(B, H_kv, n_k)) return FA_ERR_BAD_SHAPE;
   return FA_OK;
 }
 
@@ -39,6 +46,7 @@ int split_len_of(int n_k, int ns) {
 
 int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
   const long long row_chunks = ((long long)(H_q / H_kv) * T + 15) / 16;
+  if (!product_fits31(B, H_kv, row_chunks)) return 1;       // far more workgroups than CUs already
   const long long base = (long long)B * H_kv * row_chunks;  // workgroups without splitting
   // One split workgroup per CU when that leaves long splits; shorter splits go two to a CU
   // (the decode kernel fits twice), so one workgroup's start (Q and block-table loads) and
@@ -113,7 +121,7 @@ int fa_fwd_paged(const void* Q, const void* K, const void* V, void* O, float* LS
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H_q, int N_q) {
-  if (B < 1 || H_q < 1 || N_q < 1 || (long long)B * H_q * N_q > 0x7fffffffLL) return 0;  // N_q = 0: none
+  if (B < 1 || H_q < 1 || N_q < 1 || !product_fits31(B, H_q, N_q)) return 0;  // N_q = 0: none
   return fa::bwd_workspace_bytes(B, H_q, N_q);
 }
 
@@ -185,7 +193,7 @@ int check_decode(const void* Q, const void* K, const void* V, void* O, float* LS
     return FA_ERR_ALIGNMENT;
   const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
   // every partial row index (split * rows + row) must fit 32 bits, as in fa_lse_merge
-  if (ns > 1 && (long long)ns * B * H_q * T > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;
+  if (ns > 1 && (long long)B * H_q * T * ns > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;  // B*H_q*T < 2^31 here
   *ns_out = ns;
   *need_out = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
   return FA_OK;

@@ -125,6 +125,8 @@ def fwd(**kw):
     (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE), (dict(scale=float("nan")), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=float("inf")), fa.FA_ERR_BAD_SHAPE), (dict(causal=2), fa.FA_ERR_BAD_SHAPE),
     (dict(B=70000, H_q=70000, H_kv=70000), fa.FA_ERR_BAD_SHAPE),
+    # every size at its maximum: B * H * N must be rejected without the product overflowing
+    (dict(B=2**31 - 1, H_q=2**31 - 1, H_kv=2**31 - 1, N_q=2**31 - 1, N_k=2**31 - 1), fa.FA_ERR_BAD_SHAPE),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=256), fa.FA_ERR_UNSUPPORTED), (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(Q=P + 8), fa.FA_ERR_ALIGNMENT), (dict(O=P + 2), fa.FA_ERR_ALIGNMENT), (dict(LSE=P + 2), fa.FA_ERR_ALIGNMENT),
 ])
