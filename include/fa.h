@@ -6,7 +6,8 @@
  * DEVICE pointer owned by the caller.  The library never allocates, frees or synchronises:
  * each call validates its arguments, enqueues its kernels on `stream` and returns.  Outputs
  * are valid once the stream reaches the enqueued work; inputs must stay alive until then.
- * There is no global mutable state (except the scratch of fa_decode_splitkv_noalloc, below),
+ * There is no global mutable state apart from the scratch of fa_decode_splitkv_noalloc, the
+ * per-GPU placement probe result and the merge switch of the decode (below), each guarded,
  * so calls from several host threads are safe.
  *
  * Layouts (all contiguous, head dimension fastest, as the Flash Attention 1 kernel of the
@@ -157,14 +158,19 @@ int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d);
 /*
  * fa_decode_workspace_bytes -- bytes of device workspace fa_decode_splitkv needs for
  * `num_splits` splits (0 = the automatic count): the normalized partial outputs
- * O_part [ns, B*H_q*T, d] fp32 followed by LSE_part [ns, B*H_q*T] fp32, each part 256-byte
- * aligned.  Returns 0 when num_splits resolves to 1 (no workspace needed) or on bad sizes.
+ * O_part [ns, B*H_q*T, d] fp32, then LSE_part [ns, B*H_q*T] fp32, then the completion flags
+ * of the in-kernel merge, uint32 [G, ns] with G = B*H_kv*ceil(H_q/H_kv*T/16) workgroup
+ * groups, each part 256-byte aligned.  Returns 0 when num_splits resolves to 1 (no
+ * workspace needed) or on bad sizes.
  */
 size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d, int num_splits);
 
 /*
  * fa_decode_splitkv -- split-KV ("flash decoding") attention of T new queries over a cache
- * of N_k keys, with the partial results combined by the LSE merge.
+ * of N_k keys, with the partial results combined by the LSE merge: inside the decode kernel
+ * (one launch; the split of each group that completes last merges) when the GPU's
+ * workgroup placement is known (fa_decode_merge_period) and there are at most 8 splits,
+ * else by the merge kernel (fa_decode_set_merge changes this).
  *
  * Defined by: page "Attention kernel chains", chains "How many splits for decode" (the key
  * axis is cut into num_splits contiguous chunks, one worker each), "The log-sum-exp merge"
@@ -186,13 +192,49 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  *     equal length rounded up to 64 keys; trailing splits may be empty.  num_splits * B*H_q*T
  *     must stay below 2^31 (FA_ERR_BAD_SHAPE otherwise; fa_decode_workspace_bytes returns 0).
  *   workspace: >= fa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
- *     that is 0).  d == 128 or 64.
+ *     that is 0), any content: the completion flags carry a token unique to each call and
+ *     the kernel leaves them at 0, so nothing needs clearing, before the first call, between
+ *     calls or between replays of a captured call.  Afterwards O_part and LSE_part hold the
+ *     call's partials (fa_lse_merge's layout).  Calls that may overlap in time must not
+ *     share a workspace.  d == 128 or 64.
+ *   The first call with more than one split on a GPU probes its placement (below), which
+ *   synchronises `stream` once; a first call made while `stream` is being captured into a
+ *   graph skips the probe and uses the merge kernel.
  */
 int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
                       int B, int H_q, int H_kv, int T, int N_k, int d,
                       float scale, int causal, int num_splits,
                       const int32_t* block_table, int page_size, int pages_per_seq,
                       void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_decode_merge_period -- how fa_decode_splitkv merges on the GPU of `stream` (the current
+ * GPU for NULL): the placement period p > 0 when the merge runs inside the decode kernel,
+ * 0 when calls there launch the merge kernel.  The in-kernel merge relies on the GPU
+ * dealing workgroups to its XCDs round-robin, so that workgroup indices equal modulo p run
+ * on one XCD and share its L2 (the decode kernel puts all splits of a group on such
+ * indices).  The first query on a GPU (or its first split decode call) probes that: a
+ * kernel of 1024 workgroups records the XCC_ID register of each, and p is the smallest
+ * power of two <= 64 with index L always on the XCD of index L % p and indices 0 .. p-1
+ * on p different XCDs; none found: 0 for the process's lifetime.  The probe synchronises
+ * `stream` once; while `stream` is being captured it is skipped (0 for now).  Returns 0
+ * under fa_decode_set_merge(FA_MERGE_KERNEL) or on a HIP error.
+ */
+int fa_decode_merge_period(void* stream);
+
+/*
+ * fa_decode_set_merge -- process-wide choice of the decode merge: FA_MERGE_AUTO (the
+ * default: in the decode kernel where fa_decode_merge_period allows it and there are at
+ * most 8 splits, the separate merge kernel otherwise), FA_MERGE_KERNEL (always the merge
+ * kernel) or FA_MERGE_IN_KERNEL (in the decode kernel wherever the placement allows, any
+ * split count).  All give the same result up to rounding order.  Affects calls that start
+ * after it returns.  Returns the previous choice, or FA_ERR_BAD_SHAPE for another value
+ * (the choice is then unchanged).
+ */
+#define FA_MERGE_AUTO 0
+#define FA_MERGE_KERNEL 1
+#define FA_MERGE_IN_KERNEL 2
+int fa_decode_set_merge(int mode);
 
 /*
  * fa_decode_splitkv_noalloc -- fa_decode_splitkv for callers that cannot allocate device
@@ -206,9 +248,10 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
  *   split count) returns FA_ERR_WORKSPACE and enqueues nothing; FA_ERR_HIP if the scratch
  *   address cannot be looked up.  Nothing here calls hipMalloc or hipFree; the first call
  *   on a GPU looks up that GPU's copy of the array (hipGetSymbolAddress) once.
- *   Every split writes all of its partial rows before the merge reads them, so the scratch
- *   keeps no state from one call to the next that matters.  All calls on one GPU share its
- *   scratch: calls that may overlap in time on one GPU (different streams, or several
+ *   Every split writes all of its partial rows before the merge reads them and the merge
+ *   leaves the completion flags at 0, so the scratch keeps no state from one call to the
+ *   next that matters (replays of a captured call included).  All calls on one GPU share
+ *   its scratch: calls that may overlap in time on one GPU (different streams, or several
  *   host threads without ordering) race and must not be made.
  */
 #define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)

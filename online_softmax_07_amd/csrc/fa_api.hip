@@ -1,8 +1,10 @@
 // The C ABI declared in include/fa.h: argument validation, kernel selection and launch
-// on the caller's stream.  Nothing here allocates, frees or synchronises, and every check
-// runs before the first HIP call, so an invalid call enqueues nothing.
+// on the caller's stream.  Nothing here allocates or frees, every check runs before the
+// first HIP call, so an invalid call enqueues nothing, and nothing synchronises except the
+// placement probe, once per GPU, at its first split decode call (placement_period).
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "fa.h"
@@ -12,6 +14,7 @@ namespace {
 
 constexpr int kNumCU = 256;             // MI355X compute units
 constexpr int kDecodeLongSplit = 4096;  // keys: a split at least this long streams well alone on a CU
+constexpr int kInKernelMergeMaxSplits = 8;  // FA_MERGE_AUTO merges inside the decode kernel up to this
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -42,6 +45,20 @@ int check_heads(int B, int H_q, int H_kv, int n_q, int n_k, int d) {
 int split_len_of(int n_k, int ns) {
   const long long per = ((long long)n_k + ns - 1) / ns;
   return (int)((per + fa::kDecodeChunk - 1) / fa::kDecodeChunk * fa::kDecodeChunk);
+}
+
+// Workgroup groups of the decode kernel: one per (batch, KV head, 16 stacked query rows).
+size_t decode_groups(int B, int H_q, int H_kv, int T) {
+  return (size_t)B * H_kv * (((size_t)(H_q / H_kv) * T + fa::kDecodeRows - 1) / fa::kDecodeRows);
+}
+
+// A completion token unique to each decode call of the process (never 0, the value the
+// kernel leaves its flags at).
+uint32_t next_token() {
+  static std::atomic<uint32_t> counter{0x5eed0000u};
+  uint32_t t;
+  do t = counter.fetch_add(1, std::memory_order_relaxed) + 1; while (t == 0);
+  return t;
 }
 
 int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
@@ -158,7 +175,8 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * H_q * T;
   if ((long long)ns * (long long)rows > 0x7fffffffLL) return 0;  // partial index past 32 bits: rejected
-  return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float));
+  return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float)) +
+         round256((size_t)ns * decode_groups(B, H_q, H_kv, T) * sizeof(uint32_t));
 }
 
 }  // extern "C"
@@ -169,7 +187,71 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
 // (scratch_on below), and only that address is ever passed to a kernel.
 static __device__ __align__(256) unsigned char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
 
+// The placement probe's output: the XCD of each of its workgroups, per GPU (the same
+// stand-in rule as `scratch`).
+constexpr int kProbeWorkgroups = 1024;
+static __device__ __align__(256) uint32_t xcc_probe_out[kProbeWorkgroups];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// GPU of `stream` (the current GPU for a NULL stream), or -1.
+int device_of(void* stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return -1;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return -1;
+  }
+  return dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
+
+// Device address of the array `sym` on GPU `dev`, looked up with that GPU current.
+void* symbol_on(int dev, const void* sym) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, sym);
+  if (cur != dev) (void)hipSetDevice(cur);
+  return e == hipSuccess ? p : nullptr;
+}
+
+std::mutex placement_mutex;
+int placement[kMaxDevices] = {};   // 0: not probed; -1: no usable period; p > 0: period
+std::atomic<int> merge_mode{FA_MERGE_AUTO};
+
+// The period p of the workgroup-to-XCD placement on the GPU of `stream`: every workgroup
+// index L runs on the XCD of index L % p, and indices 0 .. p-1 run on p different XCDs.
+// Probed once per GPU (1024 one-wave workgroups record their XCC_ID, the caller's stream is
+// synchronised once); 0 when it cannot be known now (the stream is being captured into a
+// graph, or a HIP call failed): the caller then uses the separate merge kernel.
+int placement_period(void* stream) {
+  if (merge_mode.load(std::memory_order_relaxed) == FA_MERGE_KERNEL) return 0;
+  const int dev = device_of(stream);
+  if (dev < 0) return 0;
+  std::lock_guard<std::mutex> lock(placement_mutex);
+  if (placement[dev] != 0) return placement[dev] > 0 ? placement[dev] : 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;
+  uint32_t* d_out = static_cast<uint32_t*>(symbol_on(dev, HIP_SYMBOL(xcc_probe_out)));
+  if (d_out == nullptr) return 0;
+  uint32_t ids[kProbeWorkgroups];
+  if (fa::launch_xcc_probe(d_out, kProbeWorkgroups, stream) != hipSuccess) return 0;
+  if (hipMemcpyAsync(ids, d_out, sizeof(ids), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return 0;
+  int period = -1;
+  for (int p = 1; p <= 64 && period < 0; p *= 2) {
+    bool ok = true;
+    for (int i = 0; i < p && ok; ++i)
+      for (int j = 0; j < i && ok; ++j) ok = ids[i] != ids[j];
+    for (int L = p; L < kProbeWorkgroups && ok; ++L) ok = ids[L] == ids[L % p];
+    if (ok) period = p;
+  }
+  placement[dev] = period;
+  return period > 0 ? period : 0;
+}
 
 // Validation shared by both decode entry points; on FA_OK, *ns_out holds the resolved split
 // count and *need_out the partial-result bytes it takes (0 with one split).
@@ -208,44 +290,46 @@ int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
   const size_t rows = (size_t)B * H_q * T;
   float* O_part = nullptr;
   float* LSE_part = nullptr;
+  uint32_t* flags = nullptr;
+  int n_map = 1;
   if (ns > 1) {
-    O_part = static_cast<float*>(workspace);
-    LSE_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)ns * rows * d * sizeof(float)));
+    char* w = static_cast<char*>(workspace);
+    O_part = reinterpret_cast<float*>(w);
+    w += round256((size_t)ns * rows * d * sizeof(float));
+    LSE_part = reinterpret_cast<float*>(w);
+    w += round256((size_t)ns * rows * sizeof(float));
+    // With a known placement and few splits the kernel merges the partials itself (one
+    // launch).  Its merge waits on a chain of L2 round trips after the stream, which pays
+    // only while that chain is shorter than the merge kernel's launch and load: measured,
+    // 8 splits of the paged B=64 decode 54.5 us against 55.7, 16 splits 62.5 against 55.9,
+    // and 32 splits of the 128K-key decode 89.0 against 88.6.
+    const int mode = merge_mode.load(std::memory_order_relaxed);
+    const int p = placement_period(stream);
+    if (p > 0 && (mode == FA_MERGE_IN_KERNEL || ns <= kInKernelMergeMaxSplits)) {
+      flags = reinterpret_cast<uint32_t*>(w);
+      n_map = p;
+    }
   }
   fa::DecodeArgs a{Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, ns, split_len_of(N_k, ns),
-                   block_table, page_size, pages_per_seq, O_part, LSE_part, stream};
+                   block_table, page_size, pages_per_seq, O_part, LSE_part, flags,
+                   flags != nullptr ? next_token() : 0u, n_map, stream};
   const bool out_f32 = dtype == FA_BF16_IN_FP32_OUT;
   hipError_t e = fa::launch_decode_split(a, out_f32);
   if (e != hipSuccess) return FA_ERR_HIP;
-  if (ns > 1) e = fa::launch_lse_merge(O_part, LSE_part, O, LSE, ns, (int)rows, d, out_f32, stream);
+  if (ns > 1 && flags == nullptr) e = fa::launch_lse_merge(O_part, LSE_part, O, LSE, ns, (int)rows, d, out_f32, stream);
   return status_of(e);
 }
 
-constexpr int kMaxDevices = 64;
 std::mutex scratch_mutex;
 void* scratch_ptr[kMaxDevices] = {};
 
 // Device address of `scratch` on the GPU `stream` belongs to (the current GPU for a NULL
 // stream), looked up once per GPU with that GPU current.  NULL on any HIP error.
 void* scratch_on(void* stream) {
-  int dev = -1;
-  if (stream != nullptr) {
-    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return nullptr;
-  } else if (hipGetDevice(&dev) != hipSuccess) {
-    return nullptr;
-  }
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  const int dev = device_of(stream);
+  if (dev < 0) return nullptr;
   std::lock_guard<std::mutex> lock(scratch_mutex);
-  if (scratch_ptr[dev] == nullptr) {
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
-    void* p = nullptr;
-    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (cur != dev) (void)hipSetDevice(cur);
-    if (e != hipSuccess || p == nullptr) return nullptr;
-    scratch_ptr[dev] = p;
-  }
+  if (scratch_ptr[dev] == nullptr) scratch_ptr[dev] = symbol_on(dev, HIP_SYMBOL(scratch));
   return scratch_ptr[dev];
 }
 
@@ -283,6 +367,13 @@ int fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V, void*
   if (need > 0 && (ws = scratch_on(stream)) == nullptr) return FA_ERR_HIP;
   return run_decode(Q, K, V, O, LSE, B, H_q, H_kv, T, N_k, d, scale, causal, ns, block_table, page_size,
                     pages_per_seq, ws, dtype, stream);
+}
+
+int fa_decode_merge_period(void* stream) { return placement_period(stream); }
+
+int fa_decode_set_merge(int mode) {
+  if (mode != FA_MERGE_AUTO && mode != FA_MERGE_KERNEL && mode != FA_MERGE_IN_KERNEL) return FA_ERR_BAD_SHAPE;
+  return merge_mode.exchange(mode);
 }
 
 int fa_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE, int num_splits, int rows,

@@ -12,7 +12,9 @@
 //   * "The causal mask for a decode step": query t of the T new ones sits at position
 //     N_k - T + t and sees keys j <= N_k - T + t;
 //   * "The log-sum-exp merge": a split stores its output divided by its own sum, and the
-//     log of that sum, for the merge to weigh.
+//     log of that sum, for the merge to weigh.  With a placement map (below) the merge runs
+//     inside this kernel: the split of a group that completes last weighs the group's
+//     partials, so no second launch follows.
 //
 // Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk goes
 // to blockIdx.z).  Decode is a bytes problem, so the kernel is built around keeping loads
@@ -29,13 +31,28 @@
 // lines stream through the caches without displacing anything (on this chip that raises a
 // streaming read from about 5.8 to 6.7 TB/s).  At the end the four waves' carries are
 // merged in LDS by the LSE rule.
+//
+// Placement and the in-kernel merge.  Workgroups are dealt to the XCDs round-robin by
+// linear index, so indices equal modulo the XCD count share an XCD and its L2.  The grid is
+// one-dimensional and workgroup L takes group x + n_map * ((L / n_map) / ns) and split
+// (L / n_map) % ns, x = L % n_map: with n_map a multiple of the XCD count, all splits of a
+// group run on one XCD.  Each split stores its partial rows (plain stores, which reach that
+// L2), waits until they are complete, stores its completion flag (a token unique to the
+// call) and reads the group's flags back from the L2 (by atomics: the L1 of a CU may hold
+// a copy read by an earlier workgroup); a split that finds every flag set merges the
+// partials, read from the same L2, and returns the flags to 0.  The
+// split completing last always finds them all (two completing together both merge and
+// write the same values: the merge visits the splits in one fixed order).  No split waits
+// for another.  The host enables this only after a probe of the XCD of every workgroup
+// index has shown the round-robin placement on the GPU (flags == NULL otherwise: the
+// partials go to the separate merge kernel).
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecRows = 16;
+constexpr int kDecRows = kDecodeRows;
 constexpr int kDecChunk = 32;  // keys per wave iteration
 static_assert(kDecChunk * 2 == kDecodeChunk, "split lengths are multiples of two chunks");
 
@@ -48,11 +65,22 @@ struct DecChunk {
   u32x4 v[VL];
 };
 
+// The word at p as the L2 holds it.  Atomics run in the L2, never in a CU's L1 (which may
+// still hold a line read earlier in the kernel by another workgroup on the same CU), and a
+// compare-and-swap whose new value equals the expected one leaves memory as it is whatever
+// it finds; the compiler keeps it an atomic (an idempotent add or or becomes a plain load).
+__device__ __forceinline__ uint32_t read_at_l2(uint32_t* p) {
+  uint32_t e = 0u;
+  __hip_atomic_compare_exchange_strong(p, &e, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return e;
+}
+
 template <int D, bool PAGED, typename OutT>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, float* __restrict__ O_part,
-    float* __restrict__ LSE_part, const int32_t* __restrict__ block_table, int page_size,
+    float* __restrict__ LSE_part, uint32_t* __restrict__ flags, uint32_t token, int n_map, int n_groups,
+    int n_zc, const int32_t* __restrict__ block_table, int page_size,
     int pages_per_seq, int H_q, int H_kv, int T, int N_k, int causal, int ns, int split_len,
     float scale_log2) {
   using C = DecChunk<D>;
@@ -62,13 +90,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   constexpr int SMEM = 4 * VT_ELEMS * 2 > MERGE_BYTES ? 4 * VT_ELEMS * 2 : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-  const int split = blockIdx.x;
-  const int bk = blockIdx.y;  // b * H_kv + hk
+  // ---- which (split, group) this workgroup owns; a group is (b, hk, 16-row chunk zc) ----
+  const int wgi = blockIdx.x;
+  const int kq = wgi / n_map;
+  const int group = wgi - kq * n_map + n_map * (kq / ns);
+  if (group >= n_groups) return;            // the grid is rounded up to whole XCD rounds
+  const int split = kq % ns;
+  const int bk = group / n_zc;              // b * H_kv + hk
+  const int zc = group - bk * n_zc;
   const int b = bk / H_kv;
   const int hk = bk - b * H_kv;
   const int g = H_q / H_kv;
   const int R = g * T;                      // stacked rows of this (b, hk)
-  const int rows_total = gridDim.y * R;     // B * H_q * T
+  const int rows_total = (n_groups / n_zc) * R;  // B * H_q * T
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -76,7 +110,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   const int g4 = lane >> 4;
 
   // ---- this lane's MFMA row: (query head within the group, new token) ----
-  const int rho = blockIdx.z * kDecRows + l16;
+  const int rho = zc * kDecRows + l16;
   const bool row_ok = rho < R;
   const int hg = row_ok ? rho / T : 0;
   const int tq = row_ok ? rho - hg * T : 0;
@@ -243,73 +277,172 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   const int row = tid >> 4;        // 16 rows x 16 threads
   const int cpart = tid & 15;
   constexpr int CPT = D / 16;      // columns per thread
-  const int rr = blockIdx.z * kDecRows + row;
-  if (rr >= R) return;
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, Mw[w * kDecRows + row]);
+  const int rr = zc * kDecRows + row;
+  const bool has_row = rr < R;
   float out[CPT];
-  float lse;
-  if (M == kNegInf) {
+  float lse = kNegInf;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) out[i] = 0.f;
-    lse = kNegInf;
-  } else {
-    float wsum = 0.f, wt[4];
+  for (int i = 0; i < CPT; ++i) out[i] = 0.f;
+  if (has_row) {
+    float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wt[w] = exp2f_hw(Mw[w * kDecRows + row] - M);
-      wsum += Lw[w * kDecRows + row] * wt[w];
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, Mw[w * kDecRows + row]);
+    if (M != kNegInf) {
+      float wsum = 0.f, wt[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wt[w] = exp2f_hw(Mw[w * kDecRows + row] - M);
+        wsum += Lw[w * kDecRows + row] * wt[w];
+      }
+      const float inv = 1.f / wsum;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) a = __builtin_fmaf(Ow[(w * kDecRows + row) * D + cpart * CPT + i], wt[w], a);
+        out[i] = a * inv;
+      }
+      lse = (M + log2f_hw(wsum)) * kLn2;
     }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      float a = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) a = __builtin_fmaf(Ow[(w * kDecRows + row) * D + cpart * CPT + i], wt[w], a);
-      out[i] = a * inv;
-    }
-    lse = (M + log2f_hw(wsum)) * kLn2;
   }
-  const int rhg = rr / T;
-  const int rt = rr - rhg * T;
-  const size_t grow = ((size_t)b * H_q + hk * g + rhg) * T + rt;  // row of [B, H_q, T]
-  if (ns == 1) {
+  // rows of one group are consecutive rows of [B, H_q, T]
+  const size_t grow0 = ((size_t)b * H_q + (size_t)hk * g) * T + (size_t)zc * kDecRows;
+  const size_t grow = grow0 + row;
+  auto store_out = [&](const float (&v)[CPT], float l) {
     OutT* Orow = O + grow * D + cpart * CPT;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) Orow[i] = (OutT)out[i];
-    if (LSE != nullptr && cpart == 0) LSE[grow] = lse;
-  } else {
+    for (int i = 0; i < CPT; ++i) Orow[i] = (OutT)v[i];
+    if (LSE != nullptr && cpart == 0) LSE[grow] = l;
+  };
+  if (ns == 1) {
+    if (has_row) store_out(out, lse);
+    return;
+  }
+  if (has_row) {
     float* Orow = O_part + ((size_t)split * rows_total + grow) * D + cpart * CPT;
 #pragma unroll
     for (int i = 0; i < CPT; i += 4) *reinterpret_cast<f32x4*>(Orow + i) = f32x4{out[i], out[i + 1], out[i + 2], out[i + 3]};
     if (cpart == 0) LSE_part[(size_t)split * rows_total + grow] = lse;
   }
+  if (flags == nullptr) return;  // the merge kernel follows
+
+  // ---- the LSE merge inside the kernel (all splits of the group share this XCD's L2) ----
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have reached L2
+  __syncthreads();                                    // and every other thread's
+  int* last = reinterpret_cast<int*>(smem);           // the carries above are read: reuse
+  if (wave == 0) {
+    uint32_t* gf = flags + (size_t)group * ns;
+    if (lane == 0) gf[split] = token;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bool all = true;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int sp = s0 + lane;
+      const uint32_t f = sp < ns ? read_at_l2(gf + sp) : token;
+      all = all && !wave_any(f != token);
+    }
+    // the next call may carry the same token (a replayed graph does): leave the flags at 0
+    if (all)
+      for (int sp = lane; sp < ns; sp += 64) gf[sp] = 0u;
+    if (lane == 0) *last = all ? 1 : 0;
+  }
+  __syncthreads();
+  if (*last == 0 || !has_row) return;
+
+  // m* = max over splits of lse_s, running, in batches of 8 splits whose loads go out together.
+  // The partial rows are plain loads: a row of d floats fills whole cache lines of its own
+  // and only this group's merge reads it, so no L1 of this XCD can hold an old copy.  The
+  // lse values (4 bytes per row; other groups' rows share their lines) are read at the L2.
+  float m = kNegInf, wsum = 0.f, acc[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    f32x4 v[8][CPT / 4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(s0 + u, ns - 1);
+      const f32x4* Op = reinterpret_cast<const f32x4*>(O_part + ((size_t)sp * rows_total + grow) * D + cpart * CPT);
+#pragma unroll
+      for (int i = 0; i < CPT / 4; ++i) v[u][i] = Op[i];
+    }
+    // thread cpart of the row reads the lse of split s0 + cpart % 8; the row's 16 lanes share them
+    const int su = min(s0 + (cpart & 7), ns - 1);
+    const float mine = __uint_as_float(read_at_l2(reinterpret_cast<uint32_t*>(LSE_part + (size_t)su * rows_total + grow)));
+    float ls[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ls[u] = __shfl(mine, (lane & ~15) | u, 64);
+      if (s0 + u >= ns) ls[u] = kNegInf;   // past the last split: weight 0
+    }
+    float mb = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mb = fmaxf(mb, ls[u]);
+    const float m_new = fmaxf(m, mb);
+    // no branch on m_new: the partial loads above stay in flight with the lse loads
+    const float m_use = m_new == kNegInf ? 0.f : m_new;  // no key seen yet: every weight is 0
+    const float rescale = exp2f_hw((m - m_use) * kLog2e);  // 0 while m = -inf
+    wsum *= rescale;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) acc[i] *= rescale;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = exp2f_hw((ls[u] - m_use) * kLog2e);   // 0 for an empty split (lse -inf)
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) acc[i] = __builtin_fmaf(w, v[u][i / 4][i % 4], acc[i]);
+    }
+    m = m_new;
+  }
+  if (m == kNegInf) {                      // no split saw a key of this row: O = 0, LSE = -inf
+    store_out(acc, kNegInf);
+  } else {
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) acc[i] *= inv;
+    store_out(acc, m + log2f_hw(wsum) * kLn2);
+  }
 }
 
 template <int D, bool PAGED, typename OutT>
-static hipError_t launch_dec(const DecodeArgs& a) {
-  const int R = (a.H_q / a.H_kv) * a.T;
-  dim3 grid(a.num_splits, a.B * a.H_kv, (R + kDecRows - 1) / kDecRows);
-  hipLaunchKernelGGL((decode_split_kernel<D, PAGED, OutT>), grid, dim3(kDecThreads), 0, (hipStream_t)a.stream,
+static hipError_t launch_dec(const DecodeArgs& a, int n_zc, int n_groups, int n_map, int n_wg) {
+  hipLaunchKernelGGL((decode_split_kernel<D, PAGED, OutT>), dim3(n_wg), dim3(kDecThreads), 0, (hipStream_t)a.stream,
                      (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (OutT*)a.O, a.LSE, a.O_part,
-                     a.LSE_part, a.block_table, a.page_size, a.pages_per_seq, a.H_q, a.H_kv, a.T, a.N_k,
-                     a.causal, a.num_splits, a.split_len, a.scale * kLog2e);
+                     a.LSE_part, a.flags, a.token, n_map, n_groups, n_zc, a.block_table, a.page_size,
+                     a.pages_per_seq, a.H_q, a.H_kv, a.T, a.N_k, a.causal, a.num_splits, a.split_len,
+                     a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t dispatch_dec(const DecodeArgs& a, bool out_f32) {
+static hipError_t dispatch_dec(const DecodeArgs& a, bool out_f32, int n_zc, int n_groups, int n_map, int n_wg) {
   if (a.block_table != nullptr)
-    return out_f32 ? launch_dec<D, true, float>(a) : launch_dec<D, true, __bf16>(a);
-  return out_f32 ? launch_dec<D, false, float>(a) : launch_dec<D, false, __bf16>(a);
+    return out_f32 ? launch_dec<D, true, float>(a, n_zc, n_groups, n_map, n_wg)
+                   : launch_dec<D, true, __bf16>(a, n_zc, n_groups, n_map, n_wg);
+  return out_f32 ? launch_dec<D, false, float>(a, n_zc, n_groups, n_map, n_wg)
+                 : launch_dec<D, false, __bf16>(a, n_zc, n_groups, n_map, n_wg);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, bool out_f32) {
   const int R = (a.H_q / a.H_kv) * a.T;
-  if (a.B * (long long)a.H_kv > 65535 || (R + kDecRows - 1) / kDecRows > 65535) return hipErrorInvalidConfiguration;
-  if (a.d == 128) return dispatch_dec<128>(a, out_f32);
-  return dispatch_dec<64>(a, out_f32);
+  const long long n_zc = (R + kDecRows - 1) / kDecRows;
+  const long long n_groups = (long long)a.B * a.H_kv * n_zc;
+  const int n_map = a.flags != nullptr ? a.n_map : 1;
+  if (n_map < 1 || a.num_splits < 1) return hipErrorInvalidValue;
+  // whole rounds of n_map groups: the workgroups of a missing group return at once
+  const long long n_wg = (n_groups + n_map - 1) / n_map * n_map * a.num_splits;
+  if (n_groups > 0x7fffffffLL || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.d == 128) return dispatch_dec<128>(a, out_f32, (int)n_zc, (int)n_groups, n_map, (int)n_wg);
+  return dispatch_dec<64>(a, out_f32, (int)n_zc, (int)n_groups, n_map, (int)n_wg);
+}
+
+// ---- placement probe: the XCD (XCC_ID hardware register) of every workgroup index ----
+__global__ __launch_bounds__(64) void xcc_probe_kernel(uint32_t* out) {
+  const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 0xffffu;  // XCC_ID[15:0]
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc;
+}
+
+hipError_t launch_xcc_probe(uint32_t* out, int n_wg, void* stream) {
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(n_wg), dim3(64), 0, (hipStream_t)stream, out);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -36,6 +36,9 @@ struct DecodeArgs {
   int page_size, pages_per_seq;
   float* O_part;    // [num_splits, B*H_q*T, d] (unused when num_splits == 1)
   float* LSE_part;  // [num_splits, B*H_q*T]
+  uint32_t* flags;  // [groups, num_splits] completion flags for the in-kernel merge; NULL: merge kernel
+  uint32_t token;   // this call's completion token (never 0)
+  int n_map;        // placement period: workgroup indices equal modulo n_map share an XCD
   void* stream;
 };
 
@@ -61,6 +64,7 @@ hipError_t launch_fwd_bf16_paged(const FwdArgs& a, bool out_f32, const int32_t* 
                                  int pages_per_seq);
 hipError_t launch_fwd_fp32(const FwdArgs& a);
 hipError_t launch_decode_split(const DecodeArgs& a, bool out_f32);
+hipError_t launch_xcc_probe(uint32_t* out, int n_wg, void* stream);
 hipError_t launch_lse_merge(const float* O_part, const float* LSE_part, void* O, float* LSE,
                             int num_splits, int rows, int d, bool out_f32, void* stream);
 
@@ -68,5 +72,6 @@ size_t bwd_workspace_bytes(int B, int H_q, int N_q);
 hipError_t launch_bwd(const BwdArgs& a, bool out_f32);
 
 constexpr int kDecodeChunk = 64;  // keys per wave iteration in the decode kernel
+constexpr int kDecodeRows = 16;   // stacked query rows per decode workgroup
 
 }  // namespace fa

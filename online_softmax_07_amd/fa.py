@@ -24,7 +24,9 @@ FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, 
 FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
 
 EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-            "fa_decode_splitkv_noalloc", "fa_lse_merge", "fa_status_string", "fa_version")
+            "fa_decode_splitkv_noalloc", "fa_decode_merge_period", "fa_decode_set_merge", "fa_lse_merge",
+            "fa_status_string", "fa_version")
+FA_MERGE_AUTO, FA_MERGE_KERNEL, FA_MERGE_IN_KERNEL = 0, 1, 2   # fa_decode_set_merge choices of include/fa.h
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_DECODE_NOALLOC_SCRATCH_BYTES of include/fa.h
 
 _lib = None
@@ -70,6 +72,10 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_splitkv.restype = i
     L.fa_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, i, i, i, vp]
     L.fa_decode_splitkv_noalloc.restype = i
+    L.fa_decode_merge_period.argtypes = [vp]
+    L.fa_decode_merge_period.restype = i
+    L.fa_decode_set_merge.argtypes = [i]
+    L.fa_decode_set_merge.restype = i
     L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
     L.fa_lse_merge.restype = i
     L.fa_status_string.argtypes = [i]
@@ -339,6 +345,24 @@ def fa_decode_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                          int(page_size), int(pages_per_seq), dtype, _stream(stream, q.device))
     _raise(st, "fa_decode_splitkv_noalloc")
     return o, lse
+
+
+def fa_decode_merge_period(device=None, stream=None) -> int:
+    """Placement period the in-kernel decode merge uses on `device` (0: the merge kernel runs);
+    probes the GPU on first use."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    return int(lib().fa_decode_merge_period(_stream(stream, dev)))
+
+
+def fa_decode_set_merge(mode: int) -> int:
+    """FA_MERGE_AUTO, FA_MERGE_KERNEL or FA_MERGE_IN_KERNEL, process-wide; returns the
+    previous choice."""
+    if int(mode) not in (FA_MERGE_AUTO, FA_MERGE_KERNEL, FA_MERGE_IN_KERNEL):
+        raise FAError(FA_ERR_BAD_SHAPE, "fa_decode_set_merge")
+    st = int(lib().fa_decode_set_merge(int(mode)))
+    if st not in (FA_MERGE_AUTO, FA_MERGE_KERNEL, FA_MERGE_IN_KERNEL):
+        _raise(st, "fa_decode_set_merge")
+    return st
 
 
 def fa_lse_merge(o_part: torch.Tensor, lse_part: torch.Tensor, o: Optional[torch.Tensor] = None,

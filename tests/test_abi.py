@@ -287,11 +287,19 @@ def test_empty_calls_enqueue_nothing():
 def test_workspace_and_split_sizes():
     # one split needs no workspace
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 1) == 0
-    # ns partial rows of d fp32 plus ns lse values, each part rounded to 256 bytes
-    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == 8 * 32 * 128 * 4 + 1024
+    # ns partial rows of d fp32, then ns lse values per row, then one uint32 completion flag per
+    # split and workgroup group (batch x KV head x 16 stacked rows), each part rounded to 256 bytes
+    def r256(x):
+        return (x + 255) // 256 * 256
+
+    def ws(ns, rows, d, groups):
+        return r256(ns * rows * d * 4) + r256(ns * rows * 4) + r256(ns * groups * 4)
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == ws(8, 32, 128, 8) == 131072 + 1024 + 256
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, (1 << 26) + 1) == 0   # 32 rows x splits > 2^31
-    assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == 4 * 512 * 128 * 4 + 4 * 512 * 4
-    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == 8 * 32 * 128 * 4 + 1024  # empty cache, 8 splits
+    assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == ws(4, 512, 128, 64) == 1048576 + 8192 + 1024
+    assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == ws(8, 32, 128, 8)      # empty cache, 8 splits
+    # 2 x 40 query heads x 3 rows = 240 rows; 20 heads x 3 = 60 stacked rows per KV head -> 4 groups
+    assert fa.fa_decode_workspace_bytes(2, 40, 2, 3, 500, 64, 5) == ws(5, 240, 64, 2 * 2 * 4) == 307200 + 4864 + 512
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, -1, 128, 8) == 0                      # invalid length
     # the automatic split count aims at one wave of one workgroup on each of 256 CUs, two when
     # the splits would be short
@@ -309,3 +317,17 @@ def test_binding_refuses_host_tensors():
         fa.fa_fwd(q, q, q, o=torch.zeros_like(q), lse=torch.zeros(1, 1, 4), stream=0)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q[:, :, :3], q)
+
+
+def test_decode_merge_switch_host_side():
+    """fa_decode_set_merge is host state only: it returns the previous choice and refuses
+    anything but the three modes, leaving the choice unchanged."""
+    L = fa.lib()
+    assert L.fa_decode_set_merge(fa.FA_MERGE_KERNEL) == fa.FA_MERGE_AUTO
+    assert L.fa_decode_set_merge(fa.FA_MERGE_IN_KERNEL) == fa.FA_MERGE_KERNEL
+    for bad in (-1, 3, 1 << 30):
+        assert L.fa_decode_set_merge(bad) == fa.FA_ERR_BAD_SHAPE
+    assert L.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_IN_KERNEL
+    with pytest.raises(fa.FAError):
+        fa.fa_decode_set_merge(5)
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_AUTO

@@ -96,15 +96,43 @@ SMALL = [
     (4, 8, 1, 1, 8192, 128, True, 16, 0),
     (8, 32, 8, 4, 4096, 128, True, 16, 0),   # multi-token decode over pages: 16 stacked rows
     (2, 8, 1, 16, 2000, 64, True, 16, 0),    # 128 stacked rows, ragged last page
+    (256, 8, 1, 1, 1024, 128, True, 16, 8),  # 2048 workgroups: several splits of a group per CU in turn
 ]
 
 
+@pytest.fixture(params=["in_kernel", "merge_kernel"])
+def merge(request):
+    """Both ways of combining the splits, each for every split count: inside the decode
+    kernel and the separate merge kernel."""
+    prev = fa.fa_decode_set_merge(fa.FA_MERGE_IN_KERNEL if request.param == "in_kernel" else fa.FA_MERGE_KERNEL)
+    yield request.param
+    fa.fa_decode_set_merge(prev)
+
+
+def test_decode_merge_in_kernel_is_available():
+    # the MI355X deals workgroups to its XCDs round-robin: the probe must find that period
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_AUTO
+    p = fa.fa_decode_merge_period(DEV)
+    say("placement period", p)
+    assert p > 0 and p & (p - 1) == 0
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_KERNEL) == fa.FA_MERGE_AUTO
+    assert fa.fa_decode_merge_period(DEV) == 0
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_KERNEL
+    assert fa.fa_decode_merge_period(DEV) == p
+    with pytest.raises(fa.FAError):
+        fa.fa_decode_set_merge(7)
+    assert fa.lib().fa_decode_set_merge(7) == fa.FA_ERR_BAD_SHAPE   # through the C ABI: unchanged
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_IN_KERNEL) == fa.FA_MERGE_AUTO
+    assert fa.fa_decode_merge_period(DEV) == p
+    assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_IN_KERNEL
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
-def test_decode_small(case):
+def test_decode_small(case, merge):
     B, Hq, Hkv, T, Nk, d, causal, ps, ns = case
     w = workloads.decode(B, Hq, Hkv, T, Nk, d, seed=sum(case), causal=causal, page_size=ps,
                          num_pages=None if ps == 0 else B * (-(-Nk // ps)) + 3)
-    say("decode", case)
+    say("decode", case, merge)
     O, L = oracle_of(w)
     o, lse = run_decode(w, ns)
     check_o(o, O, "bf16")
@@ -143,14 +171,47 @@ def test_decode_workspace_needs_no_initialization():
 
 
 @pytest.mark.parametrize("ns", [255, 300])
-def test_decode_many_splits(ns):
+def test_decode_many_splits(ns, merge):
     """Hundreds of splits, each holding one 64-key piece, merged into one row per head."""
     w = workloads.decode(1, 4, 2, 1, 64 * ns, 64, seed=4700 + ns, causal=True)
-    say("decode, many splits", ns)
+    say("decode, many splits", ns, merge)
     O, L = oracle_of(w)
     o, lse = run_decode(w, ns)
     check_o(o, O, "bf16")
     check_lse(lse, L)
+
+
+def test_decode_merge_paths_agree(c5):
+    """The in-kernel merge and the merge kernel weigh the same partials: their outputs agree
+    to fp32 rounding (the two sum the splits in different orders), and the partials the
+    in-kernel call leaves in the workspace merge, through fa_lse_merge, to the same rows."""
+    w, (O, L), (q, k, v, bt) = c5
+    ns = 8
+    need = fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, ns)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    outs = {}
+    for mode in (fa.FA_MERGE_AUTO, fa.FA_MERGE_KERNEL):
+        prev = fa.fa_decode_set_merge(mode)
+        o = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+        fa.fa_decode_splitkv(q, k, v, o, lse, causal=True, scale=w.scale, num_splits=ns, block_table=bt,
+                             n_k=w.n_k, workspace=ws)
+        torch.cuda.synchronize()
+        fa.fa_decode_set_merge(prev)
+        outs[mode] = (o, lse)
+        if mode == fa.FA_MERGE_AUTO:
+            rows = 64 * 8
+            op = ws[: ns * rows * 128 * 4].view(torch.float32).view(ns, rows, 128)
+            lp = ws[ns * rows * 128 * 4: ns * rows * 128 * 4 + ns * rows * 4].view(torch.float32).view(ns, rows)
+            om, lm = fa.fa_lse_merge(op.clone(), lp.clone(), out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            torch.testing.assert_close(om.view(o.shape), o, rtol=2e-6, atol=2e-6)
+            torch.testing.assert_close(lm.view(lse.shape), lse, rtol=2e-6, atol=2e-6)
+    (oa, la), (ok_, lk) = outs[fa.FA_MERGE_AUTO], outs[fa.FA_MERGE_KERNEL]
+    torch.testing.assert_close(oa, ok_, rtol=2e-6, atol=2e-6)
+    torch.testing.assert_close(la, lk, rtol=2e-6, atol=2e-6)
+    check_o(oa, O, "fp32out")
+    check_lse(la, L)
 
 
 # ---------------------------------------------------------------------------

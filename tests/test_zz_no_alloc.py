@@ -74,3 +74,44 @@ def test_noalloc_over_the_scratch_is_refused():
     with pytest.raises(fa.FAError) as e:
         fa.fa_decode_splitkv_noalloc(q, k, v, o, None, causal=True, scale=w.scale, num_splits=ns)
     assert e.value.status == fa.FA_ERR_WORKSPACE
+
+
+def test_noalloc_graph_replays_follow_new_inputs():
+    # A captured graph replays one call with one completion token: each replay must still
+    # merge its own partials.  Paged cache, 3 sequences x 2000 tokens, 16 / 2 heads, 8 splits;
+    # new queries (and once new values) are copied in eagerly before each replay, and every
+    # replay is checked bit for bit against an eager call with a caller's workspace.
+    w = workloads.decode(3, 16, 2, 1, 2000, 128, seed=80, causal=True, page_size=16, num_pages=3 * 125 + 7)
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    bt = w.block_table.to(DEV)
+    o = torch.zeros(q.shape, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(q.shape[:3], dtype=torch.float32, device=DEV)
+    kw = dict(causal=True, scale=w.scale, num_splits=8, block_table=bt, n_k=w.n_k)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.fa_decode_splitkv_noalloc(q, k, v, o, lse, **kw)    # first call on the GPU: scratch lookup
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_decode_splitkv_noalloc(q, k, v, o, lse, **kw)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(81)
+    for r in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(DEV))
+        if r == 2:
+            v.copy_(torch.randn(v.shape, generator=gen).to(torch.bfloat16).to(DEV))
+        torch.cuda.synchronize()
+        say("graph replay", r)
+        g.replay()
+        torch.cuda.synchronize()
+        o_ref = torch.full_like(o, float("nan"))
+        l_ref = torch.full_like(lse, float("nan"))
+        fa.fa_decode_splitkv(q, k, v, o_ref, l_ref, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {r}"
+    O, L = orc.decode(host(q.cpu()), host(k.cpu()), host(v.cpu()), w.scale, True, block_table=w.block_table.numpy(),
+                      page_size=w.page_size, n_k=w.n_k)
+    check_o(o, O, "bf16")
+    check_lse(lse, L)
