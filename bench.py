@@ -8,7 +8,8 @@ Default step: one fa_fwd call on the long causal prefill B=1, H_q=H_kv=32, N=819
 largest of the prefill configurations that fit one GPU.  The headline ``value`` is its
 attention throughput in TFLOP/s (4 N^2 d per head, halved for causal) over the bracketed K
 timed calls.  ``roofline`` prices the dominant kernel's average launch (HIP events
-recorded on the stream the library launches on) against the dense bf16 MFMA peak
+recorded on the stream the library launches on, created with hipEventDisableSystemFence so
+that recording them adds no system-scope cache writeback) against the dense bf16 MFMA peak
 (prefill) or the HBM peak (decode), with ``traffic`` taken from the committed rocprofv3
 counter summary when it was measured on the current kernel source.  ``gpu_clock_mhz`` is
 the shader clock measured by one wave right before and right after the timed region;
@@ -35,11 +36,52 @@ HBM byte counters.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import statistics
 import sys
 import time
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence of hip_runtime_api.h
+
+
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, the flag HIP documents for
+    timing: recording it does not write back and invalidate the caches at system scope, a
+    cost (about 2.4 us per bracket on the paged decode) that is part of the event, not of the
+    work between two events.  Recorded on an explicit stream."""
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")   # the HIP runtime torch has loaded
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = h
+        self.e = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if HipEvent._hip.hipEventRecord(self.e, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (waits for `end`)."""
+        h = HipEvent._hip
+        ms = ctypes.c_float()
+        if h.hipEventSynchronize(end.e) != 0 or h.hipEventElapsedTime(ctypes.byref(ms), self.e, end.e) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.e:
+            HipEvent._hip.hipEventDestroy(self.e)
+
 
 METRIC = "attention TFLOP/s + % MFMA peak (prefill); HBM GB/s + % peak (decode), 1 GPU"
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -113,10 +155,9 @@ def main():
         `clocks` (a dict), the shader clock is measured right before and right after the
         bracket, outside it."""
         n_warm = warm(fn, warmup, pre, seconds)
-        st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        en = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+        st = [HipEvent() for _ in range(steps)]
+        en = [HipEvent() for _ in range(steps)]
+        t0, t1 = HipEvent(), HipEvent()
         torch.cuda.synchronize()
         if clocks is not None:
             clocks["before_timed"] = round(calib.shader_clock_mhz(dev, stream), 0)
@@ -236,10 +277,12 @@ def main():
         ms_per_step = avg   # the flush between calls is not part of the step
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, bound, peak, achieved = "GB/s", "hbm", rl.PEAK_HBM_GBPS, nbytes / (avg * 1e-3) / 1e9
-        kernel = "fa::decode_split_kernel + fa::lse_merge_kernel"
-        extra_cfg = {"T": s["T"], "num_splits": args.num_splits or fa.fa_decode_num_splits(
-            s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"]), "bytes_per_step": nbytes,
-            "paged": w.block_table is not None}
+        ns = args.num_splits or fa.fa_decode_num_splits(s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"])
+        # the library merges inside the split kernel for up to 8 splits where the placement is known
+        in_kernel = 1 < ns <= 8 and fa.fa_decode_merge_period(dev, stream) > 0
+        kernel = ("fa::decode_split_kernel (LSE merge inside)" if in_kernel or ns == 1
+                  else "fa::decode_split_kernel + fa::lse_merge_kernel")
+        extra_cfg = {"T": s["T"], "num_splits": ns, "bytes_per_step": nbytes, "paged": w.block_table is not None}
     else:
         paged = head in PAGED_PREFILL
         fn, flops, bufs = any_prefill_case(w_inputs)
@@ -278,6 +321,7 @@ def main():
                      "avg_launch_us": round(avg * 1e3, 2)},
         "gpu_clock_mhz": clocks,
         "host": host_info(),
+        "timing": "HIP events on the launch stream, created with hipEventDisableSystemFence",
     }
     traffic = load_traffic(w.name, fabuild)
     if traffic is not None:

@@ -62,6 +62,15 @@
 #ifndef FA_FWD_D128_VEARLY
 #define FA_FWD_D128_VEARLY 0     // d = 128, 1: the first of those reads are issued before the softmax
 #endif
+#ifndef FA_FWD_D64_RH
+#define FA_FWD_D64_RH 2          // d = 64, contiguous K/V: 32-row halves per wave
+#endif
+#ifndef FA_FWD_D64_WAVES
+#define FA_FWD_D64_WAVES 4       // d = 64, contiguous K/V: waves per workgroup
+#endif
+#ifndef FA_FWD_D64_BC
+#define FA_FWD_D64_BC 64         // d = 64, contiguous K/V: keys per K/V tile
+#endif
 #ifndef FA_FWD_D64_VEARLY
 #define FA_FWD_D64_VEARLY 1      // d = 64: the same (+3 % causal)
 #endif
@@ -534,8 +543,8 @@ static hipError_t launch(const FwdArgs& a, const int32_t* block_table, int page_
   // d = 128: 8 waves of 32 rows (4 waves measured 1-5 % slower).  d = 64: 4 waves of two
   // 32-row halves, so each K or V fragment read from LDS feeds two MFMAs; the registers
   // this takes fit at d = 64 only
-  constexpr int RH = D == 64 ? 2 : 1;
-  constexpr int NW = RH == 2 ? 4 : (PAGED ? 8 : FA_FWD_D128_WAVES);
+  constexpr int RH = D == 64 ? (PAGED ? 2 : FA_FWD_D64_RH) : 1;
+  constexpr int NW = D == 64 ? (PAGED ? 4 : FA_FWD_D64_WAVES) : (PAGED ? 8 : FA_FWD_D128_WAVES);
   constexpr int BR = FwdTile<D, BC, NW, RH>::BR;
   const int n_qblocks = (a.N_q + BR - 1) / BR;
   const int n_units = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;  // causal: block pairs
@@ -554,7 +563,7 @@ static hipError_t dispatch_out(const FwdArgs& a, bool out_f32, const int32_t* bt
   // key tile: 128 keys for contiguous K/V at d = 128 (half the barriers per key); 64 keys for
   // the paged variant at d = 128 (its per-lane page addressing would not fit the registers
   // otherwise) and at d = 64 (two row halves per wave)
-  constexpr int BC = (D == 128 && !PAGED) ? FA_FWD_D128_BC : 64;
+  constexpr int BC = PAGED ? 64 : (D == 128 ? FA_FWD_D128_BC : FA_FWD_D64_BC);
   if (a.causal)
     return out_f32 ? launch<D, BC, true, PAGED, float>(a, bt, ps, pps) : launch<D, BC, true, PAGED, __bf16>(a, bt, ps, pps);
   return out_f32 ? launch<D, BC, false, PAGED, float>(a, bt, ps, pps) : launch<D, BC, false, PAGED, __bf16>(a, bt, ps, pps);

@@ -224,6 +224,9 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True, varian
     # ---- trace summary ----
     bench = _last_json(tjson)
     disp = dispatches(tdir, prefixes)
+    # the members of the family this call path launched (the decode's merge kernel runs only
+    # when the split kernel does not merge by itself)
+    prefixes = [p for p in prefixes if any(r[0].startswith(p) for r in disp)]
     n_timed = bench["steps"]
     per_call = len(prefixes)
     timed = disp[-n_timed * per_call:]
