@@ -236,7 +236,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   };
 
   // ---- the stream: loads of chunk i+1 in flight while chunk i is computed; table rows
-  // (paged) fetched one chunk earlier still ----
+  // (paged) fetched one chunk earlier still, each lookup issued ahead of the K/V loads
+  // that go out with it: vector loads complete in order, so a lookup issued after them
+  // could only be used once they had all landed (measured at the paged B=64 decode: 4
+  // splits 54.9 -> 52.6 us, 8 splits 53.2 -> 52.5) ----
   if (my_chunks > 0) {
     C ca, cb_;
     int rows_next = chunk_rows(0);
@@ -246,13 +249,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     rows_after = chunk_rows(2);
     int i = 0;
     for (; i + 1 < my_chunks; i += 2) {
+      const int rows_3 = chunk_rows(i + 3);
       load(rows_next, cb_);
       rows_next = rows_after;
-      rows_after = chunk_rows(i + 3);
+      rows_after = rows_3;
       compute(i, ca);
+      const int rows_4 = chunk_rows(i + 4);
       if (i + 2 < my_chunks) load(rows_next, ca);
       rows_next = rows_after;
-      rows_after = chunk_rows(i + 4);
+      rows_after = rows_4;
       compute(i + 1, cb_);
     }
     if (i < my_chunks) compute(i, ca);
