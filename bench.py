@@ -278,8 +278,8 @@ def main():
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, bound, peak, achieved = "GB/s", "hbm", rl.PEAK_HBM_GBPS, nbytes / (avg * 1e-3) / 1e9
         ns = args.num_splits or fa.fa_decode_num_splits(s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"])
-        # the library merges inside the split kernel for up to 8 splits where the placement is known
-        in_kernel = 1 < ns <= 8 and fa.fa_decode_merge_period(dev, stream) > 0
+        in_kernel = fa.fa_decode_merge_in_kernel(s["B"], s["H_q"], s["H_kv"], s["T"], s["N_k"], s["d"], ns,
+                                                 dev, stream)
         kernel = ("fa::decode_split_kernel (LSE merge inside)" if in_kernel or ns == 1
                   else "fa::decode_split_kernel + fa::lse_merge_kernel")
         extra_cfg = {"T": s["T"], "num_splits": ns, "bytes_per_step": nbytes, "paged": w.block_table is not None}

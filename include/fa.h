@@ -149,9 +149,8 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * num_splits == 0.  Splitting pays when batch x KV heads is far below the number of
  * compute units; the aim is about one full wave of workgroups and no mostly idle second
  * wave (page "Attention kernel chains", chain "How many splits for decode"), here for the
- * MI355X's 256 compute units: one workgroup per CU, or two per CU (both resident at once)
- * when one per CU would leave splits shorter than 4096 keys.  Never more splits than
- * 256-key pieces of the cache.  Returns >= 1, or 0 on invalid sizes.
+ * MI355X's 256 compute units: one workgroup per CU.  Never more splits than 256-key pieces
+ * of the cache.  Returns >= 1, or 0 on invalid sizes.
  */
 int fa_decode_num_splits(int B, int H_q, int H_kv, int T, int N_k, int d);
 
@@ -169,7 +168,9 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  * fa_decode_splitkv -- split-KV ("flash decoding") attention of T new queries over a cache
  * of N_k keys, with the partial results combined by the LSE merge: inside the decode kernel
  * (one launch; the split of each group that completes last merges) when the GPU's
- * workgroup placement is known (fa_decode_merge_period) and there are at most 8 splits,
+ * workgroup placement is known (fa_decode_merge_period), every workgroup of the call is
+ * resident at once (at most 512) and the merging workgroup covers the splits in one round
+ * (at most 8, 16 or 32 splits for groups of more than 8, 5-8 or at most 4 stacked rows),
  * else by the merge kernel (fa_decode_set_merge changes this).
  *
  * Defined by: page "Attention kernel chains", chains "How many splits for decode" (the key
@@ -223,9 +224,18 @@ int fa_decode_splitkv(const void* Q, const void* K, const void* V, void* O, floa
 int fa_decode_merge_period(void* stream);
 
 /*
+ * fa_decode_merge_in_kernel -- whether a fa_decode_splitkv call with these sizes and
+ * num_splits (0 = automatic) on `stream`'s GPU merges inside the decode kernel (1) or
+ * launches the merge kernel or needs no merge (0); -1 on invalid sizes.  Probes the GPU's
+ * placement on first use, as fa_decode_merge_period.
+ */
+int fa_decode_merge_in_kernel(int B, int H_q, int H_kv, int T, int N_k, int d, int num_splits, void* stream);
+
+/*
  * fa_decode_set_merge -- process-wide choice of the decode merge: FA_MERGE_AUTO (the
- * default: in the decode kernel where fa_decode_merge_period allows it and there are at
- * most 8 splits, the separate merge kernel otherwise), FA_MERGE_KERNEL (always the merge
+ * default: in the decode kernel where fa_decode_merge_period allows it and the call meets
+ * the conditions under fa_decode_splitkv, the separate merge kernel otherwise),
+ * FA_MERGE_KERNEL (always the merge
  * kernel) or FA_MERGE_IN_KERNEL (in the decode kernel wherever the placement allows, any
  * split count).  All give the same result up to rounding order.  Affects calls that start
  * after it returns.  Returns the previous choice, or FA_ERR_BAD_SHAPE for another value

@@ -13,8 +13,7 @@
 namespace {
 
 constexpr int kNumCU = 256;             // MI355X compute units
-constexpr int kDecodeLongSplit = 4096;  // keys: a split at least this long streams well alone on a CU
-constexpr int kInKernelMergeMaxSplits = 8;  // FA_MERGE_AUTO merges inside the decode kernel up to this
+constexpr int kResidentDecodeWgPerCu = 2;  // decode workgroups one CU holds at once
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -61,19 +60,33 @@ uint32_t next_token() {
   return t;
 }
 
+// Whether FA_MERGE_AUTO merges inside the decode kernel: all workgroups resident at once,
+// and the merging workgroup's shares (up to 16 / rows of the group, at most 4) cover the
+// splits in one round of 8 each.  Measured (paged B=64 decode, 8/1 heads; 128K-key decode,
+// 32/8 heads; event-timed): 4 splits 51.3 us inside against the merge kernel's 52.5, 32 splits
+// of the 128K decode 86.7 against 87.6; 16 splits of the paged decode (1024 workgroups)
+// 60.4 against 54.1 and 64 splits of the 128K decode 95.8 against 90.3 lose.
+bool in_kernel_pays(int B, int H_q, int H_kv, int T, int ns) {
+  const long long rows = (long long)(H_q / H_kv) * T;
+  const long long nrow = rows < fa::kDecodeRows ? rows : fa::kDecodeRows;
+  const long long shares = nrow <= 4 ? 4 : (nrow <= 8 ? 2 : 1);
+  const double wgs = (double)decode_groups(B, H_q, H_kv, T) * ns;
+  return wgs <= (double)kNumCU * kResidentDecodeWgPerCu && ns <= 8 * shares;
+}
+
 int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
   const long long row_chunks = ((long long)(H_q / H_kv) * T + 15) / 16;
   if (!product_fits31(B, H_kv, row_chunks)) return 1;       // far more workgroups than CUs already
   const long long base = (long long)B * H_kv * row_chunks;  // workgroups without splitting
-  // One split workgroup per CU when that leaves long splits; shorter splits go two to a CU
-  // (the decode kernel fits twice), so one workgroup's start (Q and block-table loads) and
-  // end (carry merge, partial write) overlap the other's stream.  More splits than that
-  // only add partials to merge.
+  // One split workgroup per CU: one wave of workgroups, all resident, each streaming as long
+  // a split as possible.  More splits only add partials to merge.  (Two workgroups per CU for
+  // splits under 4096 keys measured better before the block-table lookups went out ahead of
+  // the K/V loads and the merge moved into the kernel; since then the paged B=64 decode takes
+  // 50.9 us at 4 splits and 52.7 us at 8.)
   const long long target = kNumCU;
   if (base < 1) return 1;  // no query row
   if (base >= target) return 1;
   long long ns = target / base;
-  if ((long long)N_k < ns * kDecodeLongSplit) ns = 2 * target / base;
   const long long max_useful = ((long long)N_k + 4 * fa::kDecodeChunk - 1) / (4 * fa::kDecodeChunk);
   if (ns > max_useful) ns = max_useful;  // at least one chunk per wave
   if (ns < 1) ns = 1;
@@ -298,14 +311,13 @@ int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
     w += round256((size_t)ns * rows * d * sizeof(float));
     LSE_part = reinterpret_cast<float*>(w);
     w += round256((size_t)ns * rows * sizeof(float));
-    // With a known placement and few splits the kernel merges the partials itself (one
-    // launch).  Its merge waits on a chain of L2 round trips after the stream, which pays
-    // only while that chain is shorter than the merge kernel's launch and load: measured,
-    // 8 splits of the paged B=64 decode 54.5 us against 55.7, 16 splits 62.5 against 55.9,
-    // and 32 splits of the 128K-key decode 89.0 against 88.6.
+    // With a known placement the kernel can merge the partials itself (one launch).  Its
+    // merge is a chain of L2 round trips after the stream, which pays while every workgroup
+    // is resident at once (no second round of workgroups waits behind a merge) and one round
+    // of 8 splits per share of the merging workgroup covers the group (in_kernel_pays).
     const int mode = merge_mode.load(std::memory_order_relaxed);
     const int p = placement_period(stream);
-    if (p > 0 && (mode == FA_MERGE_IN_KERNEL || ns <= kInKernelMergeMaxSplits)) {
+    if (p > 0 && (mode == FA_MERGE_IN_KERNEL || in_kernel_pays(B, H_q, H_kv, T, ns))) {
       flags = reinterpret_cast<uint32_t*>(w);
       n_map = p;
     }
@@ -370,6 +382,15 @@ int fa_decode_splitkv_noalloc(const void* Q, const void* K, const void* V, void*
 }
 
 int fa_decode_merge_period(void* stream) { return placement_period(stream); }
+
+int fa_decode_merge_in_kernel(int B, int H_q, int H_kv, int T, int N_k, int d, int num_splits, void* stream) {
+  if (check_heads(B, H_q, H_kv, T, N_k, d) != FA_OK || num_splits < 0) return -1;
+  const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
+  if (ns <= 1 || T == 0) return 0;
+  const int mode = merge_mode.load(std::memory_order_relaxed);
+  if (placement_period(stream) <= 0) return 0;
+  return mode == FA_MERGE_IN_KERNEL || in_kernel_pays(B, H_q, H_kv, T, ns) ? 1 : 0;
+}
 
 int fa_decode_set_merge(int mode) {
   if (mode != FA_MERGE_AUTO && mode != FA_MERGE_KERNEL && mode != FA_MERGE_IN_KERNEL) return FA_ERR_BAD_SHAPE;

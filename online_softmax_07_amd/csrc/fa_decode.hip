@@ -351,32 +351,51 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     if (lane == 0) *last = all ? 1 : 0;
   }
   __syncthreads();
-  if (*last == 0 || !has_row) return;
+  if (*last == 0) return;
 
-  // m* = max over splits of lse_s, running, in batches of 8 splits whose loads go out together.
-  // The partial rows are plain loads: a row of d floats fills whole cache lines of its own
-  // and only this group's merge reads it, so no L1 of this XCD can hold an old copy.  The
-  // lse values (4 bytes per row; other groups' rows share their lines) are read at the L2.
+  // The merge.  A group has nrow <= 16 rows; with few rows and more than 8 splits the 16 row
+  // slots of the workgroup form nsub shares (2 or 4) that divide the splits between them
+  // (share k takes splits k, k + nsub, ...), and the shares of a row then meet in LDS by the
+  // same rule.  Within a share: m* = max of lse_s, running, in rounds of 8 splits whose loads
+  // go out together.  The partial rows are plain loads: a row of d floats fills whole cache
+  // lines of its own and only this group's merge reads it, so no L1 of this XCD can hold an
+  // old copy.  The lse values (4 bytes per row; other groups' rows share their lines) are
+  // read at the L2.
+  const int nrow = min(kDecRows, R - zc * kDecRows);
+  const int nsub_rows = nrow <= 4 ? 4 : (nrow <= 8 ? 2 : 1);   // shares the row slots allow
+  const int nsub = ns <= 8 ? 1 : (ns <= 16 || nsub_rows < 4 ? min(2, nsub_rows) : 4);
+  const int rps = kDecRows / nsub;          // row slots per share
+  const int sub = row / rps;
+  const int mrow = row - sub * rps;         // the group row this thread merges
+  const bool mrow_ok = mrow < nrow;
+  const size_t mgrow = grow0 + (mrow_ok ? mrow : 0);  // clamped: slots past the rows load row 0
   float m = kNegInf, wsum = 0.f, acc[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
+  for (int s0 = sub; s0 < ns; s0 += 8 * nsub) {
     f32x4 v[8][CPT / 4];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int sp = min(s0 + u, ns - 1);
-      const f32x4* Op = reinterpret_cast<const f32x4*>(O_part + ((size_t)sp * rows_total + grow) * D + cpart * CPT);
+      const int sp = s0 + nsub * u;
 #pragma unroll
-      for (int i = 0; i < CPT / 4; ++i) v[u][i] = Op[i];
+      for (int i = 0; i < CPT / 4; ++i) v[u][i] = f32x4{};
+      if (sp < ns) {   // a round may run past the last split
+        const f32x4* Op = reinterpret_cast<const f32x4*>(O_part + ((size_t)sp * rows_total + mgrow) * D + cpart * CPT);
+#pragma unroll
+        for (int i = 0; i < CPT / 4; ++i) v[u][i] = Op[i];
+      }
     }
-    // thread cpart of the row reads the lse of split s0 + cpart % 8; the row's 16 lanes share them
-    const int su = min(s0 + (cpart & 7), ns - 1);
-    const float mine = __uint_as_float(read_at_l2(reinterpret_cast<uint32_t*>(LSE_part + (size_t)su * rows_total + grow)));
+    // lane cpart < 8 of the row reads the lse of split s0 + nsub * cpart, one atomic per
+    // (row, split) word (atomics on one word queue at the L2), and the row's 16 lanes share it
+    const int su = s0 + nsub * (cpart & 7);
+    float mine = kNegInf;
+    if (cpart < 8 && su < ns && mrow_ok)
+      mine = __uint_as_float(read_at_l2(reinterpret_cast<uint32_t*>(LSE_part + (size_t)su * rows_total + mgrow)));
     float ls[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       ls[u] = __shfl(mine, (lane & ~15) | u, 64);
-      if (s0 + u >= ns) ls[u] = kNegInf;   // past the last split: weight 0
+      if (s0 + nsub * u >= ns) ls[u] = kNegInf;   // past the last split: weight 0
     }
     float mb = kNegInf;
 #pragma unroll
@@ -397,14 +416,47 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     }
     m = m_new;
   }
-  if (m == kNegInf) {                      // no split saw a key of this row: O = 0, LSE = -inf
-    store_out(acc, kNegInf);
-  } else {
-    const float inv = 1.f / wsum;
+  auto store_row = [&](const float (&a)[CPT], float M, float W) {
+    OutT* Orow = O + mgrow * D + cpart * CPT;
+    const float inv = M == kNegInf ? 0.f : 1.f / W;   // no split saw a key: O = 0, LSE = -inf
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) acc[i] *= inv;
-    store_out(acc, m + log2f_hw(wsum) * kLn2);
+    for (int i = 0; i < CPT; ++i) Orow[i] = (OutT)(a[i] * inv);
+    if (LSE != nullptr && cpart == 0) LSE[mgrow] = M == kNegInf ? kNegInf : M + log2f_hw(W) * kLn2;
+  };
+  if (nsub == 1) {
+    if (mrow_ok) store_row(acc, m, wsum);
+    return;
   }
+  // the shares of a row meet in LDS, combined in share order (the same bits whichever split
+  // merges)
+  float* Mm = reinterpret_cast<float*>(smem);     // [16 slots]
+  float* Ws = Mm + kDecRows;                      // [16 slots]
+  float* Ac = Ws + kDecRows;                      // [16 slots][D]
+  __syncthreads();                                // every thread has read *last
+  if (cpart == 0) {
+    Mm[row] = m;
+    Ws[row] = wsum;
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; i += 4)
+    *reinterpret_cast<f32x4*>(Ac + row * D + cpart * CPT + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+  __syncthreads();
+  if (sub != 0 || !mrow_ok) return;
+  float M = kNegInf;
+  for (int k = 0; k < nsub; ++k) M = fmaxf(M, Mm[mrow + k * rps]);
+  float W = 0.f, out2[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) out2[i] = 0.f;
+  if (M != kNegInf) {
+    for (int k = 0; k < nsub; ++k) {
+      const int sl = mrow + k * rps;
+      const float wt = exp2f_hw((Mm[sl] - M) * kLog2e);   // 0 for a share that saw no key
+      W = __builtin_fmaf(Ws[sl], wt, W);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) out2[i] = __builtin_fmaf(Ac[sl * D + cpart * CPT + i], wt, out2[i]);
+    }
+  }
+  store_row(out2, M, W);
 }
 
 template <int D, bool PAGED, typename OutT>

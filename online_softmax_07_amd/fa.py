@@ -24,7 +24,8 @@ FA_OK, FA_ERR_NULL_PTR, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, 
 FA_BF16, FA_FP32, FA_BF16_IN_FP32_OUT = 0, 1, 2
 
 EXPORTED = ("fa_fwd", "fa_fwd_paged", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_num_splits", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-            "fa_decode_splitkv_noalloc", "fa_decode_merge_period", "fa_decode_set_merge", "fa_lse_merge",
+            "fa_decode_splitkv_noalloc", "fa_decode_merge_period", "fa_decode_merge_in_kernel",
+            "fa_decode_set_merge", "fa_lse_merge",
             "fa_status_string", "fa_version")
 FA_MERGE_AUTO, FA_MERGE_KERNEL, FA_MERGE_IN_KERNEL = 0, 1, 2   # fa_decode_set_merge choices of include/fa.h
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20   # FA_DECODE_NOALLOC_SCRATCH_BYTES of include/fa.h
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_splitkv_noalloc.restype = i
     L.fa_decode_merge_period.argtypes = [vp]
     L.fa_decode_merge_period.restype = i
+    L.fa_decode_merge_in_kernel.argtypes = [i, i, i, i, i, i, i, vp]
+    L.fa_decode_merge_in_kernel.restype = i
     L.fa_decode_set_merge.argtypes = [i]
     L.fa_decode_set_merge.restype = i
     L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
@@ -352,6 +355,14 @@ def fa_decode_merge_period(device=None, stream=None) -> int:
     probes the GPU on first use."""
     dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
     return int(lib().fa_decode_merge_period(_stream(stream, dev)))
+
+
+def fa_decode_merge_in_kernel(B, H_q, H_kv, T, N_k, d, num_splits=0, device=None, stream=None) -> bool:
+    """Whether a decode call of these sizes merges inside the split kernel on `device`."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    r = int(lib().fa_decode_merge_in_kernel(B, H_q, H_kv, T, N_k, d, int(num_splits), _stream(stream, dev)))
+    _need(r >= 0, "invalid decode sizes")
+    return r == 1
 
 
 def fa_decode_set_merge(mode: int) -> int:

@@ -301,10 +301,9 @@ def test_workspace_and_split_sizes():
     # 2 x 40 query heads x 3 rows = 240 rows; 20 heads x 3 = 60 stacked rows per KV head -> 4 groups
     assert fa.fa_decode_workspace_bytes(2, 40, 2, 3, 500, 64, 5) == ws(5, 240, 64, 2 * 2 * 4) == 307200 + 4864 + 512
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, -1, 128, 8) == 0                      # invalid length
-    # the automatic split count aims at one wave of one workgroup on each of 256 CUs, two when
-    # the splits would be short
+    # the automatic split count aims at one wave of one workgroup on each of 256 CUs
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 131072, 128) == 32
-    assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 8   # 2048-key splits: two workgroups per CU
+    assert fa.fa_decode_num_splits(64, 8, 1, 1, 8192, 128) == 4   # 64 groups x 4 splits
     assert fa.fa_decode_num_splits(256, 32, 8, 1, 4096, 128) == 1
     assert fa.fa_decode_num_splits(1, 32, 8, 1, 300, 128) == 2  # never more splits than 256-key pieces
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 0) == fa.fa_decode_workspace_bytes(
@@ -331,3 +330,10 @@ def test_decode_merge_switch_host_side():
     with pytest.raises(fa.FAError):
         fa.fa_decode_set_merge(5)
     assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_AUTO
+
+
+def test_decode_merge_in_kernel_rejects_bad_sizes_before_any_hip_call():
+    L = fa.lib()
+    assert L.fa_decode_merge_in_kernel(0, 8, 1, 1, 100, 128, 0, None) == -1     # B = 0
+    assert L.fa_decode_merge_in_kernel(1, 6, 4, 1, 100, 128, 0, None) == -1     # H_q % H_kv != 0
+    assert L.fa_decode_merge_in_kernel(1, 8, 1, 1, 100, 128, -3, None) == -1    # negative split count

@@ -124,7 +124,14 @@ def test_decode_merge_in_kernel_is_available():
     assert fa.lib().fa_decode_set_merge(7) == fa.FA_ERR_BAD_SHAPE   # through the C ABI: unchanged
     assert fa.fa_decode_set_merge(fa.FA_MERGE_IN_KERNEL) == fa.FA_MERGE_AUTO
     assert fa.fa_decode_merge_period(DEV) == p
+    assert fa.fa_decode_merge_in_kernel(64, 8, 1, 1, 8192, 128, 16, DEV)      # forced: any split count
     assert fa.fa_decode_set_merge(fa.FA_MERGE_AUTO) == fa.FA_MERGE_IN_KERNEL
+    # automatic: inside while every workgroup is resident and one round per share covers the splits
+    assert fa.fa_decode_merge_in_kernel(64, 8, 1, 1, 8192, 128, 0, DEV)       # 4 splits, 256 workgroups
+    assert fa.fa_decode_merge_in_kernel(1, 32, 8, 1, 131072, 128, 0, DEV)     # 32 splits, 4 shares of 8
+    assert not fa.fa_decode_merge_in_kernel(64, 8, 1, 1, 8192, 128, 16, DEV)  # 1024 workgroups
+    assert not fa.fa_decode_merge_in_kernel(1, 32, 8, 1, 131072, 128, 64, DEV)  # 64 splits > 4 x 8
+    assert not fa.fa_decode_merge_in_kernel(1, 32, 8, 1, 131072, 128, 1, DEV)   # one split: no merge
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
