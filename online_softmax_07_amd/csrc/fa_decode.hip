@@ -16,8 +16,10 @@
 //     inside this kernel: the split of a group that completes last weighs the group's
 //     partials, so no second launch follows.
 //
-// Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk goes
-// to blockIdx.z).  Decode is a bytes problem, so the kernel is built around keeping loads
+// Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk is a
+// further group); paged, two workgroups fit a CU, contiguous one (its stream keeps two
+// chunks' registers live throughout; the automatic split count aims at one wave of one
+// workgroup per CU either way).  Decode is a bytes problem, so the kernel is built around keeping loads
 // in flight: each wave streams its own 32-key chunks of the split (chunks w, w+4, ...),
 // and the loads of the next chunk are issued before the current one is computed (two
 // register sets).  K goes straight from memory into MFMA A fragments; V is written
@@ -76,7 +78,7 @@ __device__ __forceinline__ uint32_t read_at_l2(uint32_t* p) {
 }
 
 template <int D, bool PAGED, typename OutT>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
+__global__ __launch_bounds__(kDecThreads, PAGED ? 2 : 1) void decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     OutT* __restrict__ O, float* __restrict__ LSE, float* __restrict__ O_part,
     float* __restrict__ LSE_part, uint32_t* __restrict__ flags, uint32_t token, int n_map, int n_groups,
@@ -142,9 +144,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   };
   // Each lane's share of a chunk's row indices: lane l holds key (cbase + l % 32), clamped
   // into the split so every address is valid.
+  // A chunk past this wave's last one (looked up or loaded, never computed) takes the split's
+  // first key in every lane: a few cache lines instead of a whole chunk.
   auto chunk_rows = [&](int i) -> int {
-    const int ci = wave + 4 * min(i, my_chunks - 1);
-    const int key = min(k0 + ci * kDecChunk + (lane & 31), k1 - 1);
+    const int key = i < my_chunks ? min(k0 + (wave + 4 * i) * kDecChunk + (lane & 31), k1 - 1) : k0;
     return row_of(key);
   };
   auto load = [&](int rows, C& c) {
@@ -235,32 +238,61 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- the stream: loads of chunk i+1 in flight while chunk i is computed; table rows
-  // (paged) fetched one chunk earlier still, each lookup issued ahead of the K/V loads
-  // that go out with it: vector loads complete in order, so a lookup issued after them
-  // could only be used once they had all landed (measured at the paged B=64 decode: 4
-  // splits 54.9 -> 52.6 us, 8 splits 53.2 -> 52.5) ----
+  // ---- the stream: loads of chunk i+1 in flight while chunk i is computed ----
   if (my_chunks > 0) {
     C ca, cb_;
-    int rows_next = chunk_rows(0);
-    int rows_after = chunk_rows(1);
-    load(rows_next, ca);
-    rows_next = rows_after;
-    rows_after = chunk_rows(2);
-    int i = 0;
-    for (; i + 1 < my_chunks; i += 2) {
-      const int rows_3 = chunk_rows(i + 3);
-      load(rows_next, cb_);
+    if constexpr (!PAGED) {
+      // Two chunks in flight from the start and every load of the loop issued
+      // unconditionally (past-the-end chunks read one row), so every path into the loop
+      // leaves the same loads outstanding and the compiler's wait counts keep the next chunk
+      // in flight while one is computed (the 128K-key decode: 86.6 -> 84.9 us).  Both
+      // register sets are then live at once: more than 256 registers, one workgroup per CU
+      // (with many workgroups, as B=128 x 8 KV heads x 4096 keys, 0.9 % slower; B=16 x 8 x
+      // 32768 keys at 2 splits 2.2 % faster).
+      const int t0 = chunk_rows(0);
+      const int t1 = chunk_rows(1);
+      int t2 = chunk_rows(2);
+      load(t0, ca);
+      int t3 = chunk_rows(3);
+      load(t1, cb_);
+      int i = 0;
+      for (; i + 1 < my_chunks; i += 2) {
+        const int t4 = chunk_rows(i + 4);
+        compute(i, ca);
+        load(t2, ca);
+        const int t5 = chunk_rows(i + 5);
+        compute(i + 1, cb_);
+        load(t3, cb_);
+        t2 = t4;
+        t3 = t5;
+      }
+      if (i < my_chunks) compute(i, ca);
+    } else {
+      // Table rows fetched one chunk earlier still, each lookup issued ahead of the K/V loads
+      // that go out with it: vector loads complete in order, so a lookup issued after them
+      // could only be used once they had all landed (paged B=64 decode: 4 splits 54.9 -> 52.6
+      // us, 8 splits 53.2 -> 52.5).  (The contiguous loop's structure measured slower here:
+      // 50.7 -> 57.4 us.)
+      int rows_next = chunk_rows(0);
+      int rows_after = chunk_rows(1);
+      load(rows_next, ca);
       rows_next = rows_after;
-      rows_after = rows_3;
-      compute(i, ca);
-      const int rows_4 = chunk_rows(i + 4);
-      if (i + 2 < my_chunks) load(rows_next, ca);
-      rows_next = rows_after;
-      rows_after = rows_4;
-      compute(i + 1, cb_);
+      rows_after = chunk_rows(2);
+      int i = 0;
+      for (; i + 1 < my_chunks; i += 2) {
+        const int rows_3 = chunk_rows(i + 3);
+        load(rows_next, cb_);
+        rows_next = rows_after;
+        rows_after = rows_3;
+        compute(i, ca);
+        const int rows_4 = chunk_rows(i + 4);
+        if (i + 2 < my_chunks) load(rows_next, ca);
+        rows_next = rows_after;
+        rows_after = rows_4;
+        compute(i + 1, cb_);
+      }
+      if (i < my_chunks) compute(i, ca);
     }
-    if (i < my_chunks) compute(i, ca);
   }
 
   // ---- merge the four waves (same LSE rule, in base 2) ----
