@@ -19,8 +19,9 @@
 // Per workgroup: 4 waves, 16 MFMA rows (stacked heads x tokens; a further row chunk is a
 // further group); paged, two workgroups fit a CU, contiguous one (its stream keeps two
 // chunks' registers live throughout; the automatic split count aims at one wave of one
-// workgroup per CU either way).  Decode is a bytes problem, so the kernel is built around keeping loads
-// in flight: each wave streams its own 32-key chunks of the split (chunks w, w+4, ...),
+// workgroup per CU either way).  Decode is a bytes problem, so the kernel is built around
+// keeping loads in flight: each wave streams its own 32-key chunks of the split (chunks w,
+// w+4, ...),
 // and the loads of the next chunk are issued before the current one is computed (two
 // register sets).  K goes straight from memory into MFMA A fragments; V is written
 // row-major into a wave-private LDS area and read back as V^T with the transposing LDS
