@@ -39,7 +39,10 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRowBlk = 32;    // rows per LSE/D record
-constexpr int kRecPerStep = 2; // records per dK/dV step (64 query rows)
+#ifndef FA_BWD_DKDV_ROWS
+#define FA_BWD_DKDV_ROWS 64    // query rows per dK/dV step (64 or 128)
+#endif
+constexpr int kRecPerStep = FA_BWD_DKDV_ROWS / 32;  // records per dK/dV step
 
 // LSE/D records per (batch, query head): whole steps of kRecPerStep records, so a step's
 // records always exist (rows past N_q are padding with LSE = +inf, D = 0).
@@ -501,173 +504,181 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // thr = qs0 + 4hh + shift - key that is 8(i/4) + i%4 + thr >= 0.  Keys past N_k are
     // never seen.
     const bool key_ok = key < N_k;
-    auto step = [&](int s, const __bf16* qs, const __bf16* gs, const float* rs, __bf16* qs_n, __bf16* gs_n,
-                    float* rs_n) {
+    auto step = [&](int s, const __bf16* qs_step, const __bf16* gs_step, const float* rs_step, __bf16* qs_n,
+                    __bf16* gs_n, float* rs_n) {
       issue(s + 1, qs_n, gs_n, rs_n);
-      int bh, q0;
-      step_rows(s, bh, q0);
-      // One sub-block at a time (a causal step whose first sub-block sees none of this
-      // wave's keys): S = Q K^T and dP = dO V^T for its 32 rows x this wave's 32 keys,
-      auto scores = [&](int sb, f32x16& sc, f32x16& dp) {
-        const __bf16* qsb = qs + sb * 32 * D;
-        const __bf16* gsb = gs + sb * 32 * D;
-        sc = f32x16{};
-        dp = f32x16{};
+      int bh, q0_step;
+      step_rows(s, bh, q0_step);
+      // the step's rows in pairs of 32-row sub-blocks
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qsb + off.plain[t]);
-          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gsb + off.plain[t]);
-          sc = mfma32x32x16(qa, kf[t], sc);
-          dp = mfma32x32x16(ga, vf[t], dp);
-        }
-      };
-      // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf)
-      // and dS = P (dP - D[row]) as bf16 MFMA operands,
-      auto softmax = [&](int sb, const f32x16& sc, const f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
-        const int qs0 = q0 + 32 * sb;
-        const float* rsb = rs + sb * 64;
-        const int thr = qs0 + 4 * hh + shift - key;
-        f32x16 p, ds;
+      for (int pr = 0; pr < NSB / 2; ++pr) {
+        const __bf16* qs = qs_step + pr * 64 * D;
+        const __bf16* gs = gs_step + pr * 64 * D;
+        const float* rs = rs_step + pr * 128;
+        const int q0 = q0_step + 64 * pr;
+        // One sub-block at a time (a causal step whose first sub-block sees none of this
+        // wave's keys): S = Q K^T and dP = dO V^T for its 32 rows x this wave's 32 keys,
+        auto scores = [&](int sb, f32x16& sc, f32x16& dp) {
+          const __bf16* qsb = qs + sb * 32 * D;
+          const __bf16* gsb = gs + sb * 32 * D;
+          sc = f32x16{};
+          dp = f32x16{};
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rsb + 8 * gq + 4 * hh);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(rsb + 32 + 8 * gq + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * gq + e;
-            float pv = exp2f_hw(__builtin_fmaf(sc[i], scale_log2, -l4[e]));
-            const bool vis = key_ok && (!CAUSAL || 8 * gq + e + thr >= 0);
-            pv = vis ? pv : 0.f;
-            p[i] = pv;
-            ds[i] = pv * (dp[i] - d4[e]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          pf[u] = to_bf16x8(f32x8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3], p[8 * u + 4], p[8 * u + 5],
-                                  p[8 * u + 6], p[8 * u + 7]});
-          dsf[u] = to_bf16x8(f32x8{ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3], ds[8 * u + 4],
-                                   ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
-        }
-      };
-      // then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
-      auto grads = [&](int sb, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
-        const __bf16* qsb = qs + sb * 32 * D;
-        const __bf16* gsb = gs + sb * 32 * D;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            dv[cb] = mfma32x32x16(tr_frag<D>(gsb, 16 * u, off, cb), pf[u], dv[cb]);
-            dk[cb] = mfma32x32x16(tr_frag<D>(qsb, 16 * u, off, cb), dsf[u], dk[cb]);
-          }
-      };
-      static_assert(NSB == 2, "the step is written for two 32-row sub-blocks");
-      // causal: sub-block rows below wave_first_row see none of this wave's keys
-      if (!CAUSAL || q0 + 31 >= wave_first_row) {
-        // Both sub-blocks, as one software-pipelined stream of MFMAs: the scores (S, dP) of
-        // sub-blocks 0 and 1, then the gradients (dV, dK) of 0 and 1.  Each LDS operand is
-        // read PD MFMAs ahead of its use (one wave per SIMD: nothing else hides the LDS
-        // latency), and the softmax of a sub-block runs in the shadow of the MFMAs that
-        // follow its scores, EPS elements per MFMA slot in two stages (exponential, then
-        // mask and dS) one slot apart, so that each slot's VALU work is independent.  A
-        // scheduling fence after each slot keeps this order.
-        constexpr int NMS = 2 * (D / 16);  // score MFMAs per sub-block
-        constexpr int NMG = 4 * NCB;       // gradient MFMAs per sub-block
-        constexpr int NMT = 2 * NMS + 2 * NMG;
-        constexpr int PD = 2;
-        constexpr int kRecLead = 3;
-        constexpr int EPS = D >= 128 ? 1 : 2;  // softmax elements per slot
-        constexpr int NSL = 16 / EPS;          // slots of stage 1 per sub-block
-        constexpr int S0[2] = {NMS + 1, 2 * NMS + 1};  // first softmax slot of each sub-block
-        static_assert(S0[0] + 8 / EPS + 1 <= 2 * NMS && S0[0] + NSL + 1 <= 2 * NMS + 2 * NCB &&
-                          S0[1] + 8 / EPS + 1 <= 2 * NMS + NMG && S0[1] + NSL + 1 <= 2 * NMS + NMG + 2 * NCB,
-                      "each bf16 operand pair is complete before its first gradient MFMA");
-        f32x16 sc[2], dp[2];
-        float ex[2][16];
-        f32x8 p8[2], d8[2];
-        bf16x8 pf[2][2], dsf[2][2];
-        f32x4 l4[2][4], d4[2][4];
-        auto load_op = [&](auto mc) -> bf16x8 {
-          constexpr int m = decltype(mc)::value;
-          if constexpr (m < 2 * NMS) {
-            constexpr int sb = m / NMS, j = m % NMS;
-            return *reinterpret_cast<const bf16x8*>((j & 1 ? gs : qs) + sb * 32 * D + off.plain[j >> 1]);
-          } else {
-            constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
-            return tr_frag<D>((j & 1 ? qs : gs) + sb * 32 * D, 16 * (j / (2 * NCB)), off, (j >> 1) % NCB);
+          for (int t = 0; t < D / 16; ++t) {
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qsb + off.plain[t]);
+            const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gsb + off.plain[t]);
+            sc = mfma32x32x16(qa, kf[t], sc);
+            dp = mfma32x32x16(ga, vf[t], dp);
           }
         };
-        auto load_rec = [&](int sb, int gq) {
-          l4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 8 * gq + 4 * hh);
-          d4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 32 + 8 * gq + 4 * hh);
-        };
-        // register i of a sub-block holds row 8(i/4) + 4hh + i%4 of it
-        auto stage1 = [&](int sb, int i) {  // e = 2^(s scale log2e - lse2[row])
-          ex[sb][i] = exp2f_hw(__builtin_fmaf(sc[sb][i], scale_log2, -l4[sb][i >> 2][i & 3]));
-        };
-        auto stage2 = [&](auto maskc, int sb, int i) {  // P (0 past the mask), dS = P (dP - D[row])
-          float pv = ex[sb][i];
-          if constexpr (decltype(maskc)::value) {
-            const int thr = q0 + 32 * sb + 4 * hh + shift - key;
-            const bool vis = key_ok && (!CAUSAL || 8 * (i >> 2) + (i & 3) + thr >= 0);
-            pv = vis ? pv : 0.f;
+        // P = 2^(s scale log2e - lse2[row]) (0 past the mask; rows past N_q have lse2 = +inf)
+        // and dS = P (dP - D[row]) as bf16 MFMA operands,
+        auto softmax = [&](int sb, const f32x16& sc, const f32x16& dp, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+          const int qs0 = q0 + 32 * sb;
+          const float* rsb = rs + sb * 64;
+          const int thr = qs0 + 4 * hh + shift - key;
+          f32x16 p, ds;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(rsb + 8 * gq + 4 * hh);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(rsb + 32 + 8 * gq + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * gq + e;
+              float pv = exp2f_hw(__builtin_fmaf(sc[i], scale_log2, -l4[e]));
+              const bool vis = key_ok && (!CAUSAL || 8 * gq + e + thr >= 0);
+              pv = vis ? pv : 0.f;
+              p[i] = pv;
+              ds[i] = pv * (dp[i] - d4[e]);
+            }
           }
-          p8[sb][i & 7] = pv;
-          d8[sb][i & 7] = pv * (dp[sb][i] - d4[sb][i >> 2][i & 3]);
-          if ((i & 7) == 7) {
-            pf[sb][i >> 3] = to_bf16x8(p8[sb]);
-            dsf[sb][i >> 3] = to_bf16x8(d8[sb]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            pf[u] = to_bf16x8(f32x8{p[8 * u], p[8 * u + 1], p[8 * u + 2], p[8 * u + 3], p[8 * u + 4], p[8 * u + 5],
+                                    p[8 * u + 6], p[8 * u + 7]});
+            dsf[u] = to_bf16x8(f32x8{ds[8 * u], ds[8 * u + 1], ds[8 * u + 2], ds[8 * u + 3], ds[8 * u + 4],
+                                     ds[8 * u + 5], ds[8 * u + 6], ds[8 * u + 7]});
           }
         };
-        auto stream = [&](auto maskc) {
-          sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
-          bf16x8 ops[PD];
-          static_for<0, PD>([&](auto mc) { ops[decltype(mc)::value] = load_op(mc); });
-          __builtin_amdgcn_sched_barrier(0);
-          static_for<0, NMT>([&](auto mc) {
+        // then dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T through the transposing LDS read)
+        auto grads = [&](int sb, const bf16x8 (&pf)[2], const bf16x8 (&dsf)[2]) {
+          const __bf16* qsb = qs + sb * 32 * D;
+          const __bf16* gsb = gs + sb * 32 * D;
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              dv[cb] = mfma32x32x16(tr_frag<D>(gsb, 16 * u, off, cb), pf[u], dv[cb]);
+              dk[cb] = mfma32x32x16(tr_frag<D>(qsb, 16 * u, off, cb), dsf[u], dk[cb]);
+            }
+        };
+        static_assert(NSB % 2 == 0, "the step is written for pairs of 32-row sub-blocks");
+        // causal: sub-block rows below wave_first_row see none of this wave's keys
+        if (!CAUSAL || q0 + 31 >= wave_first_row) {
+          // Both sub-blocks, as one software-pipelined stream of MFMAs: the scores (S, dP) of
+          // sub-blocks 0 and 1, then the gradients (dV, dK) of 0 and 1.  Each LDS operand is
+          // read PD MFMAs ahead of its use (one wave per SIMD: nothing else hides the LDS
+          // latency), and the softmax of a sub-block runs in the shadow of the MFMAs that
+          // follow its scores, EPS elements per MFMA slot in two stages (exponential, then
+          // mask and dS) one slot apart, so that each slot's VALU work is independent.  A
+          // scheduling fence after each slot keeps this order.
+          constexpr int NMS = 2 * (D / 16);  // score MFMAs per sub-block
+          constexpr int NMG = 4 * NCB;       // gradient MFMAs per sub-block
+          constexpr int NMT = 2 * NMS + 2 * NMG;
+          constexpr int PD = 2;
+          constexpr int kRecLead = 3;
+          constexpr int EPS = D >= 128 ? 1 : 2;  // softmax elements per slot
+          constexpr int NSL = 16 / EPS;          // slots of stage 1 per sub-block
+          constexpr int S0[2] = {NMS + 1, 2 * NMS + 1};  // first softmax slot of each sub-block
+          static_assert(S0[0] + 8 / EPS + 1 <= 2 * NMS && S0[0] + NSL + 1 <= 2 * NMS + 2 * NCB &&
+                            S0[1] + 8 / EPS + 1 <= 2 * NMS + NMG && S0[1] + NSL + 1 <= 2 * NMS + NMG + 2 * NCB,
+                        "each bf16 operand pair is complete before its first gradient MFMA");
+          f32x16 sc[2], dp[2];
+          float ex[2][16];
+          f32x8 p8[2], d8[2];
+          bf16x8 pf[2][2], dsf[2][2];
+          f32x4 l4[2][4], d4[2][4];
+          auto load_op = [&](auto mc) -> bf16x8 {
             constexpr int m = decltype(mc)::value;
-            const bf16x8 a = ops[m % PD];
-            if constexpr (m + PD < NMT) ops[m % PD] = load_op(std::integral_constant<int, m + PD>{});
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq)
-                if (m == S0[sb] + 4 * gq / EPS - kRecLead) load_rec(sb, gq);
             if constexpr (m < 2 * NMS) {
               constexpr int sb = m / NMS, j = m % NMS;
-              if constexpr (j & 1) dp[sb] = mfma32x32x16(a, vf[j >> 1], dp[sb]);
-              else sc[sb] = mfma32x32x16(a, kf[j >> 1], sc[sb]);
+              return *reinterpret_cast<const bf16x8*>((j & 1 ? gs : qs) + sb * 32 * D + off.plain[j >> 1]);
             } else {
               constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
-              constexpr int u = j / (2 * NCB), cb = (j >> 1) % NCB;
-              if constexpr (j & 1) dk[cb] = mfma32x32x16(a, dsf[sb][u], dk[cb]);
-              else dv[cb] = mfma32x32x16(a, pf[sb][u], dv[cb]);
+              return tr_frag<D>((j & 1 ? qs : gs) + sb * 32 * D, 16 * (j / (2 * NCB)), off, (j >> 1) % NCB);
             }
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-              const int k = m - S0[sb];
-              if (k >= 0 && k < NSL) {
-#pragma unroll
-                for (int e = 0; e < EPS; ++e) stage1(sb, EPS * k + e);
-              }
-              if (k >= 1 && k <= NSL) {
-#pragma unroll
-                for (int e = 0; e < EPS; ++e) stage2(maskc, sb, EPS * (k - 1) + e);
-              }
+          };
+          auto load_rec = [&](int sb, int gq) {
+            l4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 8 * gq + 4 * hh);
+            d4[sb][gq] = *reinterpret_cast<const f32x4*>(rs + sb * 64 + 32 + 8 * gq + 4 * hh);
+          };
+          // register i of a sub-block holds row 8(i/4) + 4hh + i%4 of it
+          auto stage1 = [&](int sb, int i) {  // e = 2^(s scale log2e - lse2[row])
+            ex[sb][i] = exp2f_hw(__builtin_fmaf(sc[sb][i], scale_log2, -l4[sb][i >> 2][i & 3]));
+          };
+          auto stage2 = [&](auto maskc, int sb, int i) {  // P (0 past the mask), dS = P (dP - D[row])
+            float pv = ex[sb][i];
+            if constexpr (decltype(maskc)::value) {
+              const int thr = q0 + 32 * sb + 4 * hh + shift - key;
+              const bool vis = key_ok && (!CAUSAL || 8 * (i >> 2) + (i & 3) + thr >= 0);
+              pv = vis ? pv : 0.f;
             }
+            p8[sb][i & 7] = pv;
+            d8[sb][i & 7] = pv * (dp[sb][i] - d4[sb][i >> 2][i & 3]);
+            if ((i & 7) == 7) {
+              pf[sb][i >> 3] = to_bf16x8(p8[sb]);
+              dsf[sb][i >> 3] = to_bf16x8(d8[sb]);
+            }
+          };
+          auto stream = [&](auto maskc) {
+            sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+            bf16x8 ops[PD];
+            static_for<0, PD>([&](auto mc) { ops[decltype(mc)::value] = load_op(mc); });
             __builtin_amdgcn_sched_barrier(0);
-          });
-        };
-        // masking only where this wave's keys run past N_k or past the first row's reach
-        if (kw0 + 32 > N_k || (CAUSAL && kw0 + 31 > q0 + shift)) stream(std::true_type{});
-        else stream(std::false_type{});
-      } else if (q0 + 63 >= wave_first_row) {
-        f32x16 sc1, dp1;
-        bf16x8 pf1[2], ds1[2];
-        scores(1, sc1, dp1);
-        softmax(1, sc1, dp1, pf1, ds1);
-        grads(1, pf1, ds1);
+            static_for<0, NMT>([&](auto mc) {
+              constexpr int m = decltype(mc)::value;
+              const bf16x8 a = ops[m % PD];
+              if constexpr (m + PD < NMT) ops[m % PD] = load_op(std::integral_constant<int, m + PD>{});
+#pragma unroll
+              for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                  if (m == S0[sb] + 4 * gq / EPS - kRecLead) load_rec(sb, gq);
+              if constexpr (m < 2 * NMS) {
+                constexpr int sb = m / NMS, j = m % NMS;
+                if constexpr (j & 1) dp[sb] = mfma32x32x16(a, vf[j >> 1], dp[sb]);
+                else sc[sb] = mfma32x32x16(a, kf[j >> 1], sc[sb]);
+              } else {
+                constexpr int m2 = m - 2 * NMS, sb = m2 / NMG, j = m2 % NMG;
+                constexpr int u = j / (2 * NCB), cb = (j >> 1) % NCB;
+                if constexpr (j & 1) dk[cb] = mfma32x32x16(a, dsf[sb][u], dk[cb]);
+                else dv[cb] = mfma32x32x16(a, pf[sb][u], dv[cb]);
+              }
+#pragma unroll
+              for (int sb = 0; sb < 2; ++sb) {
+                const int k = m - S0[sb];
+                if (k >= 0 && k < NSL) {
+#pragma unroll
+                  for (int e = 0; e < EPS; ++e) stage1(sb, EPS * k + e);
+                }
+                if (k >= 1 && k <= NSL) {
+#pragma unroll
+                  for (int e = 0; e < EPS; ++e) stage2(maskc, sb, EPS * (k - 1) + e);
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            });
+          };
+          // masking only where this wave's keys run past N_k or past the first row's reach
+          if (kw0 + 32 > N_k || (CAUSAL && kw0 + 31 > q0 + shift)) stream(std::true_type{});
+          else stream(std::false_type{});
+        } else if (q0 + 63 >= wave_first_row) {
+          f32x16 sc1, dp1;
+          bf16x8 pf1[2], ds1[2];
+          scores(1, sc1, dp1);
+          softmax(1, sc1, dp1, pf1, ds1);
+          grads(1, pf1, ds1);
+        }
       }
       wait_vmem();
       __syncthreads();

@@ -248,7 +248,12 @@ def profile(workload, raw, summaries, steps, warmup, limit=240, run=True, varian
     for n, c, t, a, p in top_kernels(tdir):
         lines.append(f"| `{n[:110]}` | {c} | {float(t):.1f} | {float(a):.2f} | {float(p):.1f} |")
     r0 = disp[-1]
-    lines += ["", f"Registers of `{r0[0][:60]}...`: {r0[4]} VGPR, {r0[5]} AGPR, {r0[6]} SGPR; LDS {r0[7]} B.", "",
+    # rocprofv3's kernel record lists half the vector registers a wave is given on this chip
+    # (arch_vgpr_count = (VGPR + AGPR allocation) / 2, accum_vgpr_count 0): e.g. 128 for the
+    # d=128 forward, which the compiler gives 256 VGPRs
+    lines += ["", f"Registers of `{r0[0][:60]}...`: {2 * int(r0[4]) + int(r0[5])} vector registers per lane "
+              f"(VGPR and AGPR together; rocprofv3's kernel record: arch_vgpr_count {r0[4]}, accum_vgpr_count "
+              f"{r0[5]}), {r0[6]} SGPR; LDS {r0[7]} B.", "",
               f"- Mean duration per call over the {n_timed} timed calls (the last {n_timed * per_call} matching "
               f"dispatches): **{timed_us:.2f} us** -> {work / (timed_us * 1e-6) / scale:.1f} {unit}, "
               f"frac {work / (timed_us * 1e-6) / scale / peak:.4f} of {peak:g}.",
