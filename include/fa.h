@@ -191,7 +191,9 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
  *   causal: 0 (every cached key visible) or 1 (bottom-right: query t sees j <= N_k - T + t).
  *   num_splits: >= 1, or 0 for fa_decode_num_splits().  Splits are contiguous key ranges of
  *     equal length rounded up to 64 keys; trailing splits may be empty.  num_splits * B*H_q*T
- *     must stay below 2^31 (FA_ERR_BAD_SHAPE otherwise; fa_decode_workspace_bytes returns 0).
+ *     and the workgroup count, num_splits * G rounded up to a multiple of 64 groups (G as in
+ *     fa_decode_workspace_bytes), must stay below 2^31 (FA_ERR_BAD_SHAPE otherwise;
+ *     fa_decode_workspace_bytes returns 0).
  *   workspace: >= fa_decode_workspace_bytes(...) bytes of device memory (may be NULL when
  *     that is 0), any content: the completion flags carry a token unique to each call and
  *     the kernel leaves them at 0, so nothing needs clearing, before the first call, between

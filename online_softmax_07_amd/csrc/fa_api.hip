@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int kNumCU = 256;             // MI355X compute units
+constexpr int kMaxPlacementPeriod = 64;  // largest workgroup placement period the probe accepts
 constexpr int kResidentDecodeWgPerCu = 2;  // decode workgroups one CU holds at once
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -72,6 +73,13 @@ bool in_kernel_pays(int B, int H_q, int H_kv, int T, int ns) {
   const long long shares = nrow <= 4 ? 4 : (nrow <= 8 ? 2 : 1);
   const double wgs = (double)decode_groups(B, H_q, H_kv, T) * ns;
   return wgs <= (double)kNumCU * kResidentDecodeWgPerCu && ns <= 8 * shares;
+}
+
+// The decode grid (one dimension): the workgroup groups rounded up to whole placement rounds
+// of at most kMaxPlacementPeriod, times the splits, must stay below 2^31.
+bool grid_fits(int B, int H_q, int H_kv, int T, int ns) {
+  const long long groups = (long long)decode_groups(B, H_q, H_kv, T);
+  return (groups + kMaxPlacementPeriod - 1) / kMaxPlacementPeriod * kMaxPlacementPeriod * ns <= 0x7fffffffLL;
 }
 
 int auto_splits(int B, int H_q, int H_kv, int T, int N_k) {
@@ -188,6 +196,7 @@ size_t fa_decode_workspace_bytes(int B, int H_q, int H_kv, int T, int N_k, int d
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * H_q * T;
   if ((long long)ns * (long long)rows > 0x7fffffffLL) return 0;  // partial index past 32 bits: rejected
+  if (!grid_fits(B, H_q, H_kv, T, ns)) return 0;
   return round256((size_t)ns * rows * d * sizeof(float)) + round256((size_t)ns * rows * sizeof(float)) +
          round256((size_t)ns * decode_groups(B, H_q, H_kv, T) * sizeof(uint32_t));
 }
@@ -255,7 +264,7 @@ int placement_period(void* stream) {
   if (hipMemcpyAsync(ids, d_out, sizeof(ids), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return 0;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return 0;
   int period = -1;
-  for (int p = 1; p <= 64 && period < 0; p *= 2) {
+  for (int p = 1; p <= kMaxPlacementPeriod && period < 0; p *= 2) {
     bool ok = true;
     for (int i = 0; i < p && ok; ++i)
       for (int j = 0; j < i && ok; ++j) ok = ids[i] != ids[j];
@@ -282,13 +291,13 @@ int check_decode(const void* Q, const void* K, const void* V, void* O, float* LS
   }
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_BF16_IN_FP32_OUT) return FA_ERR_UNSUPPORTED;
-  if ((long long)B * H_kv > 65535 || ((long long)(H_q / H_kv) * T + 15) / 16 > 65535) return FA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (LSE && !aligned4(LSE)) ||
       (block_table && !aligned4(block_table)))
     return FA_ERR_ALIGNMENT;
   const int ns = num_splits == 0 ? auto_splits(B, H_q, H_kv, T, N_k) : num_splits;
   // every partial row index (split * rows + row) must fit 32 bits, as in fa_lse_merge
   if (ns > 1 && (long long)B * H_q * T * ns > 0x7fffffffLL) return FA_ERR_BAD_SHAPE;  // B*H_q*T < 2^31 here
+  if (!grid_fits(B, H_q, H_kv, T, ns)) return FA_ERR_BAD_SHAPE;
   *ns_out = ns;
   *need_out = fa_decode_workspace_bytes(B, H_q, H_kv, T, N_k, d, ns);
   return FA_OK;

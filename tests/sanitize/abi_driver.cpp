@@ -81,8 +81,9 @@ int main() {
                                               P, (size_t)-1, FA_BF16, nullptr), FA_ERR_BAD_SHAPE);
   expect("dec no workspace", fa_decode_splitkv(P, P, P, P, F, 1, 4, 2, 1, 100, 128, 0.1f, 1, 4, nullptr, 0, 0,
                                                nullptr, 0, FA_BF16, nullptr), FA_ERR_WORKSPACE);
-  expect("dec grid", fa_decode_splitkv(P, P, P, P, F, 300, 300, 300, 1, 100, 128, 0.1f, 1, 4, nullptr, 0, 0, P,
-                                       (size_t)-1, FA_BF16, nullptr), FA_ERR_UNSUPPORTED);
+  // one workgroup group: the grid, groups rounded up to 64 times the splits, passes 2^31
+  expect("dec grid", fa_decode_splitkv(P, P, P, P, F, 1, 1, 1, 1, 100, 128, 0.1f, 1, 1 << 25, nullptr, 0, 0, P,
+                                       (size_t)-1, FA_BF16, nullptr), FA_ERR_BAD_SHAPE);
   expect("dec table short", fa_decode_splitkv(P, P, P, P, F, 1, 4, 2, 1, 100, 128, 0.1f, 1, 4, BT, 16, 6, P,
                                               (size_t)-1, FA_BF16, nullptr), FA_ERR_BAD_SHAPE);
   expect("noalloc scratch", fa_decode_splitkv_noalloc(P, P, P, P, F, 1, 4, 2, 1, 100, 128, 0.1f, 1, 8193, nullptr, 0,

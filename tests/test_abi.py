@@ -207,7 +207,10 @@ def dec(**kw):
     (dict(bt=P, ps=0, pps=7), fa.FA_ERR_BAD_SHAPE), (dict(bt=P, ps=16, pps=0), fa.FA_ERR_BAD_SHAPE),
     (dict(bt=P, ps=16, pps=6), fa.FA_ERR_BAD_SHAPE),   # 6 * 16 < 100 keys
     (dict(d=32), fa.FA_ERR_UNSUPPORTED), (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
-    (dict(B=300, H_q=300, H_kv=300), fa.FA_ERR_UNSUPPORTED),   # B*H_kv beyond the grid's y range
+    # the one-dimensional grid takes any B*H_kv: this call gets as far as the workspace check
+    (dict(B=300, H_q=300, H_kv=300), fa.FA_ERR_WORKSPACE),
+    # a split count whose workgroup count, groups rounded up to 64 times the splits, passes 2^31
+    (dict(H_q=1, H_kv=1, ns=1 << 25, wsb=1 << 62), fa.FA_ERR_BAD_SHAPE),
     (dict(K=P + 4), fa.FA_ERR_ALIGNMENT), (dict(bt=P + 2, ps=16, pps=7), fa.FA_ERR_ALIGNMENT),
     (dict(ws=None), fa.FA_ERR_WORKSPACE), (dict(wsb=100), fa.FA_ERR_WORKSPACE), (dict(ns=0, N_k=100000, wsb=10), fa.FA_ERR_WORKSPACE),
     (dict(ws=P + 4), fa.FA_ERR_ALIGNMENT),
@@ -296,6 +299,9 @@ def test_workspace_and_split_sizes():
         return r256(ns * rows * d * 4) + r256(ns * rows * 4) + r256(ns * groups * 4)
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, 8) == ws(8, 32, 128, 8) == 131072 + 1024 + 256
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 131072, 128, (1 << 26) + 1) == 0   # 32 rows x splits > 2^31
+    # one group: the grid (groups rounded up to 64, times the splits) passes 2^31 first
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 1, 100, 128, 1 << 25) == 0         # 64 x 2^25 = 2^31
+    assert fa.fa_decode_workspace_bytes(1, 1, 1, 1, 100, 128, (1 << 25) - 1) > 0
     assert fa.fa_decode_workspace_bytes(64, 8, 1, 1, 8192, 128, 4) == ws(4, 512, 128, 64) == 1048576 + 8192 + 1024
     assert fa.fa_decode_workspace_bytes(1, 32, 8, 1, 0, 128, 8) == ws(8, 32, 128, 8)      # empty cache, 8 splits
     # 2 x 40 query heads x 3 rows = 240 rows; 20 heads x 3 = 60 stacked rows per KV head -> 4 groups

@@ -188,6 +188,23 @@ def test_decode_many_splits(ns, merge):
     check_lse(lse, L)
 
 
+def test_decode_groups_past_16_bits():
+    """More workgroup groups than a 16-bit grid dimension holds (70000 sequences of one KV head
+    with two query heads each): the one-dimensional grid reaches every one.  Sampled sequences,
+    at both ends and around 2^16, are compared with the oracle; every row must be finite."""
+    B, Hq, Hkv, T, Nk, d = 70000, 2, 1, 1, 40, 64
+    w = workloads.decode(B, Hq, Hkv, T, Nk, d, seed=4900, causal=True)
+    q, k, v = (t.to(DEV) for t in (w.q, w.k, w.v))
+    idx = [0, 1, 4095, 65534, 65535, 65536, 65537, B - 1]
+    O, L = orc.decode(host(w.q[idx]), host(w.k[idx]), host(w.v[idx]), w.scale, True)
+    for ns in (1, 2):
+        say("decode, 70000 groups, num_splits", ns)
+        o, lse = run_decode(w, ns, q=q, k=k, v=v)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        check_o(o[idx], O, "bf16")
+        check_lse(lse[idx], L)
+
+
 def test_decode_merge_paths_agree(c5):
     """The in-kernel merge and the merge kernel weigh the same partials: their outputs agree
     to fp32 rounding (the two sum the splits in different orders), and the partials the
