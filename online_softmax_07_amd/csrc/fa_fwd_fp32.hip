@@ -17,17 +17,18 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows32) void fwd_fp32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int H_q, int H_kv, int N_q, int N_k,
-    float scale_log2) {
+    float scale_log2, int n_rblocks) {
   __shared__ float Qs[kRows32][D + 1];
   __shared__ __attribute__((aligned(16))) float Ks[kKeys32][D];
   __shared__ __attribute__((aligned(16))) float Vs[kKeys32][D];
 
-  const int bh = blockIdx.x;
+  // one-dimensional grid: (batch, head) major, then the 64-row block
+  const int bh = blockIdx.x / n_rblocks;
   const int b = bh / H_q;
   const int h = bh - b * H_q;
   const int hk = h / (H_q / H_kv);
   const int tid = threadIdx.x;
-  const int q0 = blockIdx.y * kRows32;
+  const int q0 = (blockIdx.x - bh * n_rblocks) * kRows32;
   const int row = q0 + tid;
   const int shift = N_k - N_q;
   const float* Qp = Q + (size_t)bh * N_q * D;
@@ -106,15 +107,16 @@ __global__ __launch_bounds__(kRows32) void fwd_fp32_kernel(
 
 template <int D, bool CAUSAL>
 static hipError_t launch32(const FwdArgs& a) {
-  dim3 grid(a.B * a.H_q, (a.N_q + kRows32 - 1) / kRows32);
-  hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL>), grid, dim3(kRows32), 0, (hipStream_t)a.stream,
+  const int n_rb = (a.N_q + kRows32 - 1) / kRows32;
+  const long long total = (long long)a.B * a.H_q * n_rb;  // <= B*H_q*N_q < 2^31 (checked by the caller)
+  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(kRows32), 0, (hipStream_t)a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.LSE,
-                     a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e);
+                     a.H_q, a.H_kv, a.N_q, a.N_k, a.scale * kLog2e, n_rb);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_fp32(const FwdArgs& a) {
-  if ((a.N_q + kRows32 - 1) / kRows32 > 65535) return hipErrorInvalidConfiguration;
   if (a.d == 128) return a.causal ? launch32<128, true>(a) : launch32<128, false>(a);
   return a.causal ? launch32<64, true>(a) : launch32<64, false>(a);
 }

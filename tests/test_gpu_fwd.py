@@ -70,6 +70,21 @@ def test_fp32_cases(B, Hq, Hkv, Nq, Nk, d, causal):
     check_lse(lse, L, tol=1e-5)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_more_row_blocks_than_16_bits(causal):
+    """N_q of 2^16 64-row blocks and more (4.19 million rows; the grid is one-dimensional),
+    against the oracle on sampled rows around each 2^16-block boundary.  Causal with
+    N_q > N_k: only the last N_k rows see a key, every other row must be O = 0, LSE = -inf."""
+    n_q, n_k, d = 65536 * 64 + 100, 8, 64
+    w = workloads.prefill(1, 1, 1, n_q, n_k, d, seed=1100 + causal, causal=causal, dtype="fp32")
+    say("fp32, 4.19M rows, causal", causal)
+    o, lse = run_fwd(w)
+    idx = np.array([0, 1, 65535 * 64, 65536 * 64 - 1, 65536 * 64, n_q - n_k - 1, n_q - n_k, n_q - 1])
+    O, L = orc.attention(host(w.q), host(w.k), host(w.v), w.scale, causal, rows=idx)
+    check_o(o[:, :, idx], O, "fp32")
+    check_lse(lse[:, :, idx], L, tol=1e-5)
+
+
 # ---------------------------------------------------------------------------
 # bf16 MFMA path, every element
 # ---------------------------------------------------------------------------
