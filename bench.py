@@ -13,7 +13,8 @@ that recording them adds no system-scope cache writeback) against the dense bf16
 (prefill) or the HBM peak (decode), with ``traffic`` taken from the committed rocprofv3
 counter summary when it was measured on the current kernel source.  ``gpu_clock_mhz`` is
 the shader clock measured by one wave right before and right after the timed region;
-``calib`` the ceilings of the committed calibration kernels (an MFMA-only loop and a
+``calib`` the ceilings of the committed calibration kernels (an MFMA-only loop, the same
+loop with fp32 FMAs issued by the same waves, and a
 one-pass streaming read) measured after everything else; ``host`` the CPU model.
 ``breakdown`` adds the other prefill variants (including B=4, H=16, N=4096 at d=128 and
 d=64), the chunked prefill over a paged cache (FLOPs: 4 d per visible query-key pair,
@@ -380,10 +381,12 @@ def main():
     if not args.no_calib:
         flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         mf = calib.mfma_ceiling(dev, stream)
+        mix = calib.mfma_valu_mix(dev, stream)
         sr = calib.stream_read_ceiling(dev, stream, flush=flush_caches)
         del flush
         result["calib"] = {
             "mfma_loop": {**mf, "frac_of_peak": round(mf["tflops"] / rl.PEAK_BF16_MFMA_TFLOPS, 4)},
+            "mfma_valu_mix": mix,
             "stream_read": {**sr, "frac_of_peak": round(sr["GB/s"] / rl.PEAK_HBM_GBPS, 4)},
         }
         ceiling = mf["tflops"] if unit == "TFLOP/s" else sr["GB/s"]

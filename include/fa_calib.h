@@ -31,6 +31,17 @@ extern "C" {
 int fa_calib_mfma(float* sink, uint64_t* cycles, int blocks, int iters, void* stream);
 
 /*
+ * fa_calib_mfma_valu -- how far vector work hides under matrix work when the same waves
+ * issue both, as in the attention loops: the workgroups of fa_calib_mfma, each wave running
+ * `iters` rounds of (mfma ? four 32x32x16 bf16 MFMAs : nothing) followed by `fmas` fp32
+ * FMAs in eight independent chains.  mfma in {0, 1}, fmas in {0, 24, 48}, not both 0
+ * (mfma = 1, fmas = 0 is the loop of fa_calib_mfma).  Time the three variants of one
+ * `fmas` count: if the vector work hid completely, mixed = MFMA-only; if not at all,
+ * mixed = MFMA-only + FMA-only.  Same buffers and return codes as fa_calib_mfma.
+ */
+int fa_calib_mfma_valu(float* sink, uint64_t* cycles, int blocks, int iters, int mfma, int fmas, void* stream);
+
+/*
  * fa_calib_stream_read -- the HBM read ceiling for a one-pass stream, in the access
  * pattern of the decode kernel: `blocks` workgroups of 256 threads read `bytes` bytes of
  * `buf` once, 16 bytes per lane per load, two loads in flight per lane, nontemporal

@@ -48,6 +48,51 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 1) void mfma_loop_kernel(float* si
   }
 }
 
+// The matrix core and the vector unit sharing a SIMD: the MFMA loop above with `fmas` fp32
+// FMAs after each round's four MFMAs, in eight independent chains (FMAS = 0: MFMAs only;
+// MFMA = false: the FMAs only).  Comparing the three times shows how much of the vector work
+// hides under the matrix work when both come from the same waves, as in the attention loops.
+template <bool MFMA, int FMAS>
+__global__ __launch_bounds__(64 * kMfmaWaves, 1) void mix_loop_kernel(float* sink, uint64_t* cycles, int iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)((float)(threadIdx.x & 63) * 0.001f);
+    b[i] = (__bf16)((float)i * 0.01f);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)threadIdx.x * 0.01f + (float)i;
+  const float fa = 0.999f, fb = 0.001f * (float)(blockIdx.x & 7);
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MFMA) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int f = 0; f < FMAS; ++f) x[f & 7] = __builtin_fmaf(x[f & 7], fa, fb);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    cycles[2 * blockIdx.x] = t1 - t0;
+    cycles[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 // Every thread reads items gid, gid + stride, ... < n16 (16 bytes each), two in flight.
 __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const u32x4* __restrict__ in, size_t n16,
                                                                      float* sink) {
@@ -87,6 +132,20 @@ int fa_calib_mfma(float* sink, uint64_t* cycles, int blocks, int iters, void* st
   if (blocks < 1 || iters < 1) return 2;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(64 * kMfmaWaves), 0, (hipStream_t)stream, sink, cycles,
                      iters);
+  return launched();
+}
+
+int fa_calib_mfma_valu(float* sink, uint64_t* cycles, int blocks, int iters, int mfma, int fmas, void* stream) {
+  if (sink == nullptr || cycles == nullptr) return 1;
+  if (blocks < 1 || iters < 1 || (mfma != 0 && mfma != 1) || (fmas != 0 && fmas != 24 && fmas != 48) ||
+      (mfma == 0 && fmas == 0))
+    return 2;
+  auto k = mix_loop_kernel<true, 24>;
+  if (mfma && fmas == 0) k = mix_loop_kernel<true, 0>;
+  else if (mfma && fmas == 48) k = mix_loop_kernel<true, 48>;
+  else if (!mfma && fmas == 24) k = mix_loop_kernel<false, 24>;
+  else if (!mfma && fmas == 48) k = mix_loop_kernel<false, 48>;
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(64 * kMfmaWaves), 0, (hipStream_t)stream, sink, cycles, iters);
   return launched();
 }
 

@@ -55,7 +55,7 @@ def test_calib_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", fabuild.CALIB_LIB], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     names = declared_functions(CALIB_HEADER)
-    assert names == ["fa_calib_clock", "fa_calib_mfma", "fa_calib_stream_read"]
+    assert names == ["fa_calib_clock", "fa_calib_mfma", "fa_calib_mfma_valu", "fa_calib_stream_read"]
     for name in names:
         assert name in exported, name
         assert hasattr(L, name)
@@ -67,6 +67,12 @@ def test_calib_rejects_before_any_launch():
     assert L.fa_calib_mfma(None, P, 1, 1, None) == 1
     assert L.fa_calib_mfma(P, P, 0, 1, None) == 2
     assert L.fa_calib_mfma(P, P, 1, 0, None) == 2
+    assert L.fa_calib_mfma_valu(None, P, 1, 1, 1, 24, None) == 1
+    assert L.fa_calib_mfma_valu(P, P, 0, 1, 1, 24, None) == 2
+    assert L.fa_calib_mfma_valu(P, P, 1, 0, 1, 24, None) == 2
+    assert L.fa_calib_mfma_valu(P, P, 1, 1, 2, 24, None) == 2    # mfma is 0 or 1
+    assert L.fa_calib_mfma_valu(P, P, 1, 1, 1, 12, None) == 2    # fmas is 0, 24 or 48
+    assert L.fa_calib_mfma_valu(P, P, 1, 1, 0, 0, None) == 2     # no work at all
     assert L.fa_calib_stream_read(None, 16, P, 1, None) == 1
     assert L.fa_calib_stream_read(P, 24, P, 1, None) == 2      # not a multiple of 16
     assert L.fa_calib_stream_read(P + 8, 16, P, 1, None) == 2   # not 16-byte aligned
